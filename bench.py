@@ -1,0 +1,264 @@
+#!/usr/bin/env python3
+"""Benchmark of the stable LSD radix sort on one MI355X.
+
+One step = one whole sort call (every pass: upsweep, scan, downsweep) of the
+workload's input, already resident in HBM, into a preallocated output with
+preallocated temp storage.  Default workload: 1e8 uint32 keys drawn uniformly
+from [0, 2^32) with seed 1, keys only, bits [0, 32), 4 passes of 8-bit digits.
+
+Prints one JSON line with the throughput (Gkeys/s), the dominant kernel's
+roofline figures (from HIP events around each launch, on the launch stream)
+and the CPU oracle timed on a bounded sample of the same input.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import statistics
+import sys
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published peak
+PAGES_GPU_GKEYS = 6.25         # 1e8 32-bit ints in ~16 ms (quant67.com survey, sections 9.3-9.4)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "downsweep_traffic.txt")
+
+
+def log(msg: str) -> None:
+    sys.stderr.write(msg + "\n")
+    sys.stderr.flush()
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def kernel_source_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in ("sorting_lsd_radix_sort_amd/csrc/kernels.hpp", "sorting_lsd_radix_sort_amd/csrc/lrsort.hip"):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per downsweep launch from the committed rocprofv3 counter
+    summary, if it was taken on this workload with the current kernel source."""
+    try:
+        fields = {}
+        with open(TRAFFIC_FILE) as f:
+            for ln in f:
+                if ":" in ln and not ln.startswith("#"):
+                    k, v = ln.split(":", 1)
+                    fields[k.strip()] = v.strip()
+        if fields.get("kernel_source_digest") != kernel_source_digest():
+            return None
+        if fields.get("workload") != workload:
+            return None
+        return float(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="c2_u32_keys_1e8")
+    ap.add_argument("--cpu-sample", type=int, default=1 << 25,
+                    help="keys of the input the CPU oracle sorts for the baseline")
+    ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        log("bench.py measures one GPU only: this sort runs on a single MI355X and has no "
+            "multi-GPU path (requested --gpus %d)." % args.gpus)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import sorting_lsd_radix_sort_amd as lrs
+    from sorting_lsd_radix_sort_amd import inputs
+
+    cfg = inputs.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("[bench] drawing %s (n=%d)" % (cfg.name, cfg.n))
+    keys_np = inputs.draw_keys(cfg)
+    vals_np = inputs.draw_values(cfg)
+    n = keys_np.size
+    ksz = keys_np.dtype.itemsize
+    vsz = 4 if vals_np is not None else 0
+    passes = (cfg.end_bit - cfg.begin_bit + 7) // 8
+
+    kin = torch.from_numpy(keys_np).to(dev)
+    kout = torch.empty_like(kin)
+    vin = torch.from_numpy(vals_np).to(dev) if vals_np is not None else None
+    vout = torch.empty_like(vin) if vin is not None else None
+    sfx = {"u32": "u32", "f32": "f32", "u64": "u64"}[cfg.key_type]
+    if vin is None:
+        fn = getattr(lrs, "lrs_sort_keys_" + sfx)
+        arrays = (kin, kout)
+    else:
+        fn = getattr(lrs, "lrs_sort_pairs_" + sfx)
+        arrays = (kin, vin, kout, vout)
+    temp_bytes = fn(None, 0, *arrays, n, cfg.begin_bit, cfg.end_bit)
+    temp = torch.empty(temp_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        fn(temp, temp_bytes, *arrays, n, cfg.begin_bit, cfg.end_bit, stream)
+
+    log("[bench] warmup %d" % args.warmup)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps, events on the launch stream
+    log("[bench] timing %d steps" % args.steps)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    total_ms = ev[0].elapsed_time(ev[-1])
+    per_step = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    ms_per_step = total_ms / args.steps
+    gkeys = n / (ms_per_step * 1e-3) / 1e9
+
+    # ---- sanity check of the last output (ordered, same multiset sum)
+    if cfg.key_type == "f32":
+        ko = kout.view(torch.int32)
+        f = kout
+        ordered = bool((f[1:] >= f[:-1]).all().item())
+        same_sum = bool(torch.equal(kin.view(torch.int32).to(torch.int64).sum(), ko.to(torch.int64).sum()))
+    else:
+        width = 64 if cfg.key_type == "u64" else 32
+        as_i = kout.view(torch.int64 if width == 64 else torch.int32)
+        mask = (1 << (cfg.end_bit - cfg.begin_bit)) - 1
+        if width == 32:
+            w = (as_i.to(torch.int64) & 0xFFFFFFFF) >> cfg.begin_bit
+            w = w & mask
+            ordered = bool((w[1:] >= w[:-1]).all().item())
+        else:
+            hi = (as_i >> 32) & 0xFFFFFFFF
+            lo = as_i & 0xFFFFFFFF
+            ordered = bool(((hi[1:] > hi[:-1]) | ((hi[1:] == hi[:-1]) & (lo[1:] >= lo[:-1]))).all().item())
+        src_i = kin.view(as_i.dtype)
+        same_sum = bool(torch.equal((src_i.to(torch.int64) & 0xFFFF).sum(), (as_i.to(torch.int64) & 0xFFFF).sum()))
+    if vout is not None:
+        same_sum = same_sum and int(vout.to(torch.int64).sum().item()) == n * (n - 1) // 2
+    log("[bench] output ordered=%s multiset-sum=%s" % (ordered, same_sum))
+
+    # ---- per-kernel durations: same K steps again with events around each launch
+    log("[bench] per-kernel events over %d steps" % args.steps)
+    lrs.lrs_prof_start(args.steps * 3 * passes + 16)
+    try:
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        lrs.lrs_prof_stop()
+        recs = [lrs.lrs_prof_read(i) for i in range(lrs.lrs_prof_count())]
+    finally:
+        lrs.lrs_prof_release()
+    by_kind = {}
+    for kind, ms in recs:
+        by_kind.setdefault(lrs.KERNEL_NAMES[kind], []).append(ms)
+    avg = {k: sum(v) / len(v) for k, v in by_kind.items()}
+    launches = {k: len(v) for k, v in by_kind.items()}
+
+    # algorithmic bytes: upsweep reads K*n; downsweep reads and writes (K+V)*n;
+    # the whole sort moves P*(3K+2V)*n (strict reading P*(2K+2V)*n)
+    down_bytes = 2 * (ksz + vsz) * n
+    up_bytes = ksz * n
+    achieved = down_bytes / (avg["downsweep"] * 1e-3) / 1e9
+    sort_bytes = passes * (3 * ksz + 2 * vsz) * n
+    strict_bytes = passes * (2 * ksz + 2 * vsz) * n
+
+    # ---- device copy of the key array, the achievable streaming reference
+    copy_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for _ in range(2):
+        lrs.lrs_device_copy(kout, kin, n * ksz, stream)
+    copy_ev[0].record(stream)
+    for _ in range(args.steps):
+        lrs.lrs_device_copy(kout, kin, n * ksz, stream)
+    copy_ev[1].record(stream)
+    torch.cuda.synchronize()
+    copy_ms = copy_ev[0].elapsed_time(copy_ev[1]) / args.steps
+    copy_gbs = 2 * n * ksz / (copy_ms * 1e-3) / 1e9
+
+    workload = cfg.name
+    traffic = measured_traffic(workload)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        m = min(args.cpu_sample, n)
+        sample_k = np.ascontiguousarray(keys_np[:m])
+        sample_v = None if vals_np is None else np.arange(m, dtype=np.uint32)
+        log("[bench] CPU oracle on %d keys x %d runs" % (m, args.cpu_reps))
+        times = oracle.time_sort(sample_k, sample_v, cfg.begin_bit, cfg.end_bit, reps=args.cpu_reps)
+        t = statistics.median(times)
+        cpu = {"value": m / t / 1e9, "unit": "Gkeys/s", "cores": 1, "kind": "oracle",
+               "sample": "first %d keys of the same input, %s, median of %d runs, one host thread "
+                         "of %d (%s)" % (m, "pairs" if vals_np is not None else "keys only",
+                                         args.cpu_reps, os.cpu_count() or 0, cpu_model()),
+               "seconds": t}
+
+    result = {
+        "metric": "Gkeys/s, uint32 LSD radix sort at 1e8 keys; % of HBM roofline",
+        "value": gkeys,
+        "unit": "Gkeys/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": (gkeys / PAGES_GPU_GKEYS) if cfg.name == "c2_u32_keys_1e8" else None,
+        "dtype": cfg.key_type if vals_np is None else cfg.key_type + "+u32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "description": cfg.description, "n": n,
+                   "key": cfg.key_type, "values": "u32" if vals_np is not None else None,
+                   "begin_bit": cfg.begin_bit, "end_bit": cfg.end_bit, "passes": passes,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "downsweep", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic, "bytes_per_launch": down_bytes,
+                     "avg_launch_ms": avg["downsweep"]},
+        "kernels_avg_ms": avg,
+        "kernel_launches": launches,
+        "upsweep_gbs": up_bytes / (avg["upsweep"] * 1e-3) / 1e9,
+        "sort_roofline": {"bytes": sort_bytes, "gbs": sort_bytes / (ms_per_step * 1e-3) / 1e9,
+                          "frac": sort_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                          "strict_bytes": strict_bytes,
+                          "strict_frac": strict_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "step_ms_median": statistics.median(per_step),
+        "step_ms_min": min(per_step),
+        "copy_reference_gbs": copy_gbs,
+        "output_checked": ordered and same_sum,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+    return 0 if (ordered and same_sum) else 1
+
+
+if __name__ == "__main__":
+    sys.exit(main())

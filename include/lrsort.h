@@ -1,0 +1,112 @@
+/*
+ * lrsort.h -- C ABI of a stable LSD radix sort for AMD MI355X (gfx950).
+ *
+ * The operation: sort n keys (and, for the pair calls, a uint32 value carried
+ * with each key) ascending by the key bits [begin_bit, end_bit), from an input
+ * array into an output array, stably (equal bit fields keep their input order).
+ * The bit range is half-open, as in the library call of the page "GPU radix
+ * sort: from the CUB implementation to performance tuning", section 2, and the
+ * sort runs one pass per 8-bit digit from least to most significant, each pass a
+ * histogram, a scan and a scatter (same page, section 3).  A last digit narrower
+ * than 8 bits sorts only the bits left before end_bit (the quant67.com survey
+ * "Parallel sorting: from merge networks to GPU bitonic sort", section 8.1:
+ * the last few bits take one counting step).  Bits outside [begin_bit,
+ * end_bit) play no part in the order but are kept in the output keys.
+ *
+ * Keys and values move together in one sort, never as a key sort followed by a
+ * gather (same page, section 5.5).
+ *
+ * Float32 keys are ordered through the sign-flip encoding of the kwkr.cn essay
+ * on bitonic vs. LSD radix sort, section 3.3 (non-negative floats: set the sign
+ * bit; negative floats: invert every bit), applied on the first load and undone
+ * on the last store; for them [begin_bit, end_bit) indexes the encoded word.
+ * Under it -0.0 sorts before +0.0, +NaN after +inf and -NaN before -inf; bit
+ * patterns come back unchanged.
+ *
+ * Conventions shared by every sort call:
+ *  - Two-phase temp storage (same page, section 2, and section 6, first
+ *    pitfall): with d_temp == NULL the call writes the bytes it needs to
+ *    *temp_bytes, returns LRS_OK and does no work.  Call it with the same
+ *    pointers, n and bit range as the real call (in-place use can need more
+ *    temp).  With d_temp != NULL, *temp_bytes is the size of d_temp; less than
+ *    the requirement gives LRS_ERR_TEMP_TOO_SMALL and nothing is touched.
+ *  - All array pointers are device memory owned by the caller.  The library
+ *    allocates nothing, keeps no state between calls, and enqueues its kernels
+ *    on `stream` asynchronously: results are ready when the stream reaches
+ *    them.  d_temp must stay allocated until then.
+ *  - The input arrays are not modified, except when the caller passes the same
+ *    pointer for input and output (in-place sort, same page section 6, third
+ *    pitfall), which is allowed for keys and values independently.  Partial
+ *    overlap of an input and an output gives LRS_ERR_INVALID_ARG; overlap of
+ *    d_temp with any array is undefined.
+ *  - 0 <= begin_bit <= end_bit <= 8 * sizeof(key); otherwise
+ *    LRS_ERR_INVALID_ARG.  begin_bit == end_bit copies input to output.
+ *  - 0 <= n <= 2^32 - 1 (offsets are 32-bit); n == 0 is a no-op.  Otherwise
+ *    LRS_ERR_INVALID_ARG.
+ *  - Arrays must be aligned to their element size; NULL array pointers with
+ *    n > 0 give LRS_ERR_INVALID_ARG.
+ *  - Ascending only.  The result is deterministic (identical on every run).
+ *  - A failed kernel launch gives LRS_ERR_HIP.
+ *  - Calls on different streams with different temp buffers may run
+ *    concurrently; a temp buffer must not be shared by calls in flight.
+ */
+#ifndef LRSORT_H
+#define LRSORT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum lrs_status {
+    LRS_OK = 0,
+    LRS_ERR_INVALID_ARG = 1,
+    LRS_ERR_TEMP_TOO_SMALL = 2,
+    LRS_ERR_HIP = 3
+} lrs_status;
+
+/* Keys-only sorts: d_keys_in[0..n) -> d_keys_out[0..n). */
+lrs_status lrs_sort_keys_u32(void *d_temp, size_t *temp_bytes,
+                             const uint32_t *d_keys_in, uint32_t *d_keys_out,
+                             int64_t n, int begin_bit, int end_bit, hipStream_t stream);
+lrs_status lrs_sort_keys_u64(void *d_temp, size_t *temp_bytes,
+                             const uint64_t *d_keys_in, uint64_t *d_keys_out,
+                             int64_t n, int begin_bit, int end_bit, hipStream_t stream);
+lrs_status lrs_sort_keys_f32(void *d_temp, size_t *temp_bytes,
+                             const float *d_keys_in, float *d_keys_out,
+                             int64_t n, int begin_bit, int end_bit, hipStream_t stream);
+
+/* Pair sorts: (d_keys_in[i], d_values_in[i]) move together to the outputs.
+ * Argument order follows the pair call of the page "GPU radix sort ...",
+ * section 5.5. */
+lrs_status lrs_sort_pairs_u32(void *d_temp, size_t *temp_bytes,
+                              const uint32_t *d_keys_in, const uint32_t *d_values_in,
+                              uint32_t *d_keys_out, uint32_t *d_values_out,
+                              int64_t n, int begin_bit, int end_bit, hipStream_t stream);
+lrs_status lrs_sort_pairs_u64(void *d_temp, size_t *temp_bytes,
+                              const uint64_t *d_keys_in, const uint32_t *d_values_in,
+                              uint64_t *d_keys_out, uint32_t *d_values_out,
+                              int64_t n, int begin_bit, int end_bit, hipStream_t stream);
+lrs_status lrs_sort_pairs_f32(void *d_temp, size_t *temp_bytes,
+                              const float *d_keys_in, const uint32_t *d_values_in,
+                              float *d_keys_out, uint32_t *d_values_out,
+                              int64_t n, int begin_bit, int end_bit, hipStream_t stream);
+
+/* Static description of a status code (never NULL). */
+const char *lrs_status_string(lrs_status status);
+
+/* Plain device-to-device copy of `bytes` bytes on `stream` with the library's
+ * own streaming kernel (the sort uses it when begin_bit == end_bit).  Also the
+ * achievable-bandwidth reference a benchmark times beside the sort.  dst and
+ * src must not overlap.  LRS_ERR_INVALID_ARG for NULL pointers with bytes > 0. */
+lrs_status lrs_device_copy(void *d_dst, const void *d_src, size_t bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LRSORT_H */

@@ -1,1 +1,240 @@
-"""lrsort: a stable LSD radix sort for AMD MI355X (gfx950)."""
+"""lrsort: a stable LSD radix sort for AMD MI355X (gfx950).
+
+Python binding of the C ABI in ``include/lrsort.h`` (ctypes).  Every function
+named ``lrs_*`` here takes the same arguments as the C function of the same name
+and only marshals them: device pointers may be given as ints or as torch device
+tensors, the stream as an int handle, a ``torch.cuda.Stream`` or None (torch's
+current stream).  All sorting work runs in the HIP kernels of ``liblrsort.so``;
+there is no fallback, and a missing library raises.
+
+``sort_keys`` / ``sort_pairs`` are conveniences over the same calls that
+allocate outputs and temp storage as torch tensors.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "liblrsort.so")
+
+LRS_OK = 0
+LRS_ERR_INVALID_ARG = 1
+LRS_ERR_TEMP_TOO_SMALL = 2
+LRS_ERR_HIP = 3
+
+KERNEL_NAMES = {0: "upsweep", 1: "scan", 2: "downsweep", 3: "copy"}
+
+SORT_FUNCTIONS = ("lrs_sort_keys_u32", "lrs_sort_keys_u64", "lrs_sort_keys_f32",
+                  "lrs_sort_pairs_u32", "lrs_sort_pairs_u64", "lrs_sort_pairs_f32")
+EXPORTED = SORT_FUNCTIONS + ("lrs_status_string", "lrs_device_copy", "lrs_prof_start",
+                             "lrs_prof_stop", "lrs_prof_count", "lrs_prof_read",
+                             "lrs_prof_release")
+
+
+class LrsError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s" % (where, status_string(status)))
+
+
+_lib = None
+
+
+def load_library() -> ctypes.CDLL:
+    """Loads liblrsort.so from the package directory (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("liblrsort.so is not built; run `python -m sorting_lsd_radix_sort_amd.build` "
+                           "(or __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz, i64, ci = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int64, ctypes.c_int
+    psz = ctypes.POINTER(ctypes.c_size_t)
+    for name in SORT_FUNCTIONS:
+        fn = getattr(lib, name)
+        if "_pairs_" in name:
+            fn.argtypes = [vp, psz, vp, vp, vp, vp, i64, ci, ci, vp]
+        else:
+            fn.argtypes = [vp, psz, vp, vp, i64, ci, ci, vp]
+        fn.restype = ci
+    lib.lrs_status_string.argtypes = [ci]
+    lib.lrs_status_string.restype = ctypes.c_char_p
+    lib.lrs_device_copy.argtypes = [vp, vp, sz, vp]
+    lib.lrs_device_copy.restype = ci
+    lib.lrs_prof_start.argtypes = [ci]
+    lib.lrs_prof_start.restype = ci
+    lib.lrs_prof_stop.argtypes = []
+    lib.lrs_prof_stop.restype = ci
+    lib.lrs_prof_count.argtypes = []
+    lib.lrs_prof_count.restype = ci
+    lib.lrs_prof_read.argtypes = [ci, ctypes.POINTER(ci), ctypes.POINTER(ctypes.c_float)]
+    lib.lrs_prof_read.restype = ci
+    lib.lrs_prof_release.argtypes = []
+    lib.lrs_prof_release.restype = ci
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().lrs_status_string(int(status)).decode()
+
+
+def lrs_status_string(status: int) -> str:
+    return status_string(status)
+
+
+def _ptr(x) -> int | None:
+    """Device pointer of an int, None, or a torch tensor (which must be on a GPU)."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x or None
+    if hasattr(x, "data_ptr"):
+        if not x.is_cuda:
+            raise ValueError("lrsort needs device tensors, got a tensor on %s" % x.device)
+        return x.data_ptr()
+    raise TypeError("cannot take a device pointer of %r" % type(x))
+
+
+def _stream(s) -> int | None:
+    if isinstance(s, int):
+        return s or None
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream or None
+    return s.cuda_stream or None
+
+
+def _check(status: int, where: str) -> None:
+    if status != LRS_OK:
+        raise LrsError(status, where)
+
+
+def _sort_call(name, d_temp, temp_bytes, arrays, n, begin_bit, end_bit, stream):
+    lib = load_library()
+    tb = ctypes.c_size_t(int(temp_bytes or 0))
+    temp = _ptr(d_temp)
+    st = None if temp is None else _stream(stream)
+    status = getattr(lib, name)(temp, ctypes.byref(tb), *[_ptr(a) for a in arrays], int(n),
+                                int(begin_bit), int(end_bit), st)
+    _check(status, name)
+    return tb.value
+
+
+def _make_keys(name):
+    def fn(d_temp, temp_bytes, d_keys_in, d_keys_out, n, begin_bit, end_bit, stream=None):
+        """Calls the C function of the same name.  With d_temp None returns the
+        temp bytes needed; otherwise enqueues the sort and returns temp_bytes.
+        Raises LrsError on a non-OK status."""
+        return _sort_call(name, d_temp, temp_bytes, (d_keys_in, d_keys_out), n, begin_bit, end_bit,
+                          stream)
+    fn.__name__ = name
+    return fn
+
+
+def _make_pairs(name):
+    def fn(d_temp, temp_bytes, d_keys_in, d_values_in, d_keys_out, d_values_out, n, begin_bit,
+           end_bit, stream=None):
+        """Calls the C function of the same name (see the keys-only variants)."""
+        return _sort_call(name, d_temp, temp_bytes, (d_keys_in, d_values_in, d_keys_out, d_values_out),
+                          n, begin_bit, end_bit, stream)
+    fn.__name__ = name
+    return fn
+
+
+lrs_sort_keys_u32 = _make_keys("lrs_sort_keys_u32")
+lrs_sort_keys_u64 = _make_keys("lrs_sort_keys_u64")
+lrs_sort_keys_f32 = _make_keys("lrs_sort_keys_f32")
+lrs_sort_pairs_u32 = _make_pairs("lrs_sort_pairs_u32")
+lrs_sort_pairs_u64 = _make_pairs("lrs_sort_pairs_u64")
+lrs_sort_pairs_f32 = _make_pairs("lrs_sort_pairs_f32")
+
+
+def lrs_device_copy(d_dst, d_src, nbytes: int, stream=None) -> None:
+    _check(load_library().lrs_device_copy(_ptr(d_dst), _ptr(d_src), int(nbytes), _stream(stream)),
+           "lrs_device_copy")
+
+
+# ---------------------------------------------------------------- profiling
+
+def lrs_prof_start(capacity: int) -> None:
+    _check(load_library().lrs_prof_start(int(capacity)), "lrs_prof_start")
+
+
+def lrs_prof_stop() -> None:
+    load_library().lrs_prof_stop()
+
+
+def lrs_prof_count() -> int:
+    return int(load_library().lrs_prof_count())
+
+
+def lrs_prof_read(i: int) -> tuple[int, float]:
+    kind = ctypes.c_int(0)
+    ms = ctypes.c_float(0.0)
+    _check(load_library().lrs_prof_read(int(i), ctypes.byref(kind), ctypes.byref(ms)), "lrs_prof_read")
+    return kind.value, ms.value
+
+
+def lrs_prof_release() -> None:
+    load_library().lrs_prof_release()
+
+
+# ------------------------------------------------------------- conveniences
+
+_KEY_SUFFIX = {"torch.uint32": "u32", "torch.uint64": "u64", "torch.float32": "f32"}
+KEY_BITS = {"u32": 32, "u64": 64, "f32": 32}
+
+
+def key_suffix(dtype) -> str:
+    try:
+        return _KEY_SUFFIX[str(dtype)]
+    except KeyError:
+        raise TypeError("lrsort sorts uint32, uint64 or float32 keys, not %s" % dtype) from None
+
+
+def _temp_tensor(nbytes, device, temp):
+    import torch
+    if temp is not None and temp.numel() * temp.element_size() >= nbytes:
+        return temp
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def sort_keys(keys, begin_bit: int = 0, end_bit: int | None = None, out=None, temp=None, stream=None):
+    """Stable ascending sort of a 1-D device tensor of uint32/uint64/float32 keys
+    over bits [begin_bit, end_bit); returns the output tensor."""
+    import torch
+    sfx = key_suffix(keys.dtype)
+    end_bit = KEY_BITS[sfx] if end_bit is None else end_bit
+    keys = keys.contiguous()
+    if out is None:
+        out = torch.empty_like(keys)
+    fn = globals()["lrs_sort_keys_" + sfx]
+    need = fn(None, 0, keys, out, keys.numel(), begin_bit, end_bit)
+    t = _temp_tensor(need, keys.device, temp)
+    fn(t, t.numel() * t.element_size(), keys, out, keys.numel(), begin_bit, end_bit, stream)
+    return out
+
+
+def sort_pairs(keys, values, begin_bit: int = 0, end_bit: int | None = None, keys_out=None,
+               values_out=None, temp=None, stream=None):
+    """Stable ascending pair sort (uint32 values); returns (keys_out, values_out)."""
+    import torch
+    sfx = key_suffix(keys.dtype)
+    if str(values.dtype) != "torch.uint32":
+        raise TypeError("values must be uint32, not %s" % values.dtype)
+    end_bit = KEY_BITS[sfx] if end_bit is None else end_bit
+    keys = keys.contiguous()
+    values = values.contiguous()
+    if keys_out is None:
+        keys_out = torch.empty_like(keys)
+    if values_out is None:
+        values_out = torch.empty_like(values)
+    fn = globals()["lrs_sort_pairs_" + sfx]
+    n = keys.numel()
+    need = fn(None, 0, keys, values, keys_out, values_out, n, begin_bit, end_bit)
+    t = _temp_tensor(need, keys.device, temp)
+    fn(t, t.numel() * t.element_size(), keys, values, keys_out, values_out, n, begin_bit, end_bit, stream)
+    return keys_out, values_out

@@ -1,0 +1,535 @@
+// lrsort.hip -- host side of the C ABI in include/lrsort.h: argument checks,
+// pass plan, temp-storage layout and kernel launches on the caller's stream.
+//
+// A sort over [begin_bit, end_bit) runs P = ceil((end_bit - begin_bit) / 8)
+// passes, pass p sorting by bits [begin_bit + 8p, min(begin_bit + 8p + 8,
+// end_bit)) (the page "GPU radix sort: from the CUB implementation to
+// performance tuning", section 2: one call over [0, 32) equals four 8-bit calls
+// with the source and destination swapped after each).  Each pass enqueues
+// upsweep -> scan -> downsweep with no host synchronization.
+//
+// Buffers: pass 0 reads the input and the last pass writes the output; the
+// passes in between ping-pong through an alternate buffer A in temp storage, the
+// first destination being chosen by the parity of P so that the last pass lands
+// in the output (same page, section 6, third pitfall: know which buffer holds
+// the last pass).  When input and output are the same array and P is odd, pass 0
+// cannot write the output it is still reading, so a second alternate buffer B is
+// used (P >= 3) or the result is copied from A (P == 1).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <mutex>
+#include <vector>
+
+#include "kernels.hpp"
+#include "lrsort.h"
+#include "lrsort_prof.h"
+
+#define LRS_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+using namespace lrs;
+
+enum KeyKind { KIND_U32 = 0, KIND_F32 = 1, KIND_U64 = 2 };
+
+constexpr int kMaxBlocks = 4096;  // count-matrix width cap (scan: 256 threads x 16)
+constexpr int kUpsweepThreads = 256;
+constexpr int kScanThreads = 256;
+constexpr int kScanPerThread = kMaxBlocks / kScanThreads;
+constexpr size_t kAlign = 256;
+
+// Downsweep tile shapes (waves per workgroup x keys per lane).
+constexpr int kWaves32 = 4, kItems32 = 16;  // 4096-key tiles for 32-bit keys
+constexpr int kWaves64 = 4, kItems64 = 16;  // 4096-key tiles for 64-bit keys
+
+int tile_keys(KeyKind kind) { return kind == KIND_U64 ? kWaves64 * 64 * kItems64 : kWaves32 * 64 * kItems32; }
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// ------------------------------------------------------------------ profiling
+
+struct Prof {
+    bool on = false;
+    int cap = 0;
+    int count = 0;
+    std::vector<hipEvent_t> ev;  // 2 per record
+    std::vector<int> kind;
+};
+Prof g_prof;
+
+template <typename F>
+hipError_t launch(int kind, hipStream_t stream, F &&f)
+{
+    const bool rec = g_prof.on && g_prof.count < g_prof.cap;
+    if (rec) (void)hipEventRecord(g_prof.ev[2 * g_prof.count], stream);
+    f();
+    hipError_t err = hipGetLastError();
+    if (rec) {
+        (void)hipEventRecord(g_prof.ev[2 * g_prof.count + 1], stream);
+        g_prof.kind[g_prof.count] = kind;
+        g_prof.count++;
+    }
+    return err;
+}
+
+// --------------------------------------------------------------- device info
+
+struct DevInfo {
+    bool ready = false;
+    int cus = 0;
+};
+std::mutex g_dev_mu;
+DevInfo g_dev[64];
+
+hipError_t device_cus(int *cus)
+{
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_dev_mu);
+    if (!g_dev[dev].ready) {
+        int n = 0;
+        err = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+        if (err != hipSuccess) return err;
+        g_dev[dev].cus = n;
+        g_dev[dev].ready = true;
+    }
+    *cus = g_dev[dev].cus;
+    return hipSuccess;
+}
+
+// Resident workgroups per CU of a kernel (cached per kernel and device).
+template <typename Kern>
+hipError_t occupancy(Kern kern, int threads, int *per_cu)
+{
+    static std::mutex mu;
+    static int cache[64] = {0};
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cache[dev] == 0) {
+        int nb = 0;
+        err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, threads, 0);
+        if (err != hipSuccess) return err;
+        cache[dev] = nb > 0 ? nb : 1;
+    }
+    *per_cu = cache[dev];
+    return hipSuccess;
+}
+
+// -------------------------------------------------------------------- plan
+
+enum Buf { BUF_IN = 0, BUF_OUT = 1, BUF_A = 2, BUF_B = 3 };
+
+struct Plan {
+    int passes = 0;
+    int dst[64];
+    bool need_a = false;
+    bool need_b = false;
+    bool copy_a_to_out = false;
+};
+
+Plan make_plan(int passes, bool in_place)
+{
+    Plan pl;
+    pl.passes = passes;
+    if (passes == 0) return pl;
+    if (!in_place || passes % 2 == 0) {
+        for (int p = 0; p < passes; ++p) pl.dst[p] = ((passes - 1 - p) % 2 == 0) ? BUF_OUT : BUF_A;
+        pl.need_a = passes >= 2;
+        return pl;
+    }
+    pl.need_a = true;
+    if (passes == 1) {
+        pl.dst[0] = BUF_A;
+        pl.copy_a_to_out = true;
+        return pl;
+    }
+    pl.need_b = true;
+    pl.dst[0] = BUF_A;
+    pl.dst[1] = BUF_B;
+    for (int p = 2; p < passes; ++p) pl.dst[p] = ((passes - 1 - p) % 2 == 0) ? BUF_OUT : BUF_B;
+    return pl;
+}
+
+bool overlap_partial(const void *a, const void *b, size_t bytes)
+{
+    if (a == b || bytes == 0) return false;
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + bytes && y < x + bytes;
+}
+
+struct Request {
+    KeyKind kind;
+    const void *keys_in;
+    void *keys_out;
+    const uint32_t *vals_in;  // NULL for keys only
+    uint32_t *vals_out;
+    int64_t n;
+    int begin_bit, end_bit;
+};
+
+struct Layout {
+    int passes = 0;
+    int tile = 0;
+    int64_t tiles = 0;
+    int max_blocks = 0;
+    Plan kplan, vplan;
+    size_t off_counts = 0, off_rowtot = 0, off_ka = 0, off_kb = 0, off_va = 0, off_vb = 0;
+    size_t total = 0;
+};
+
+Layout make_layout(const Request &rq)
+{
+    Layout L;
+    const size_t ksz = rq.kind == KIND_U64 ? 8 : 4;
+    L.passes = (rq.end_bit - rq.begin_bit + kRadixBits - 1) / kRadixBits;
+    L.tile = tile_keys(rq.kind);
+    L.tiles = (rq.n + L.tile - 1) / L.tile;
+    L.max_blocks = (int)std::min<int64_t>(L.tiles, kMaxBlocks);
+    L.kplan = make_plan(L.passes, rq.keys_in == rq.keys_out);
+    L.vplan = make_plan(L.passes, rq.vals_in != nullptr && rq.vals_in == rq.vals_out);
+    size_t off = 0;
+    L.off_counts = off;
+    off += align_up((size_t)kRadix * L.max_blocks * 4);
+    L.off_rowtot = off;
+    off += align_up((size_t)kRadix * 4);
+    const size_t kbytes = align_up((size_t)rq.n * ksz), vbytes = align_up((size_t)rq.n * 4);
+    if (L.kplan.need_a) { L.off_ka = off; off += kbytes; }
+    if (L.kplan.need_b) { L.off_kb = off; off += kbytes; }
+    if (rq.vals_in) {
+        if (L.vplan.need_a) { L.off_va = off; off += vbytes; }
+        if (L.vplan.need_b) { L.off_vb = off; off += vbytes; }
+    }
+    L.total = off;
+    return L;
+}
+
+lrs_status copy_bytes(void *dst, const void *src, size_t bytes, hipStream_t stream)
+{
+    if (bytes == 0 || dst == src) return LRS_OK;
+    const uintptr_t d = (uintptr_t)dst, s = (uintptr_t)src;
+    hipError_t err;
+    if ((d % 16) == 0 && (s % 16) == 0) {
+        const int64_t n16 = (int64_t)(bytes / 16);
+        if (n16 > 0) {
+            const int grid = (int)std::min<int64_t>((n16 + 255) / 256, 8192);
+            err = launch(LRS_KERNEL_COPY, stream, [&] {
+                copy16_kernel<<<grid, 256, 0, stream>>>((const uint4 *)src, (uint4 *)dst, n16);
+            });
+            if (err != hipSuccess) return LRS_ERR_HIP;
+        }
+        const size_t done = (size_t)n16 * 16;
+        if (done < bytes) {
+            err = launch(LRS_KERNEL_COPY, stream, [&] {
+                copy1_kernel<<<1, 256, 0, stream>>>((const uint8_t *)src + done, (uint8_t *)dst + done,
+                                                   (int64_t)(bytes - done));
+            });
+            if (err != hipSuccess) return LRS_ERR_HIP;
+        }
+        return LRS_OK;
+    }
+    const int grid = (int)std::min<int64_t>(((int64_t)bytes + 255) / 256, 8192);
+    err = launch(LRS_KERNEL_COPY, stream, [&] {
+        copy1_kernel<<<grid, 256, 0, stream>>>((const uint8_t *)src, (uint8_t *)dst, (int64_t)bytes);
+    });
+    return err == hipSuccess ? LRS_OK : LRS_ERR_HIP;
+}
+
+// ------------------------------------------------------------ pass launchers
+
+template <typename K, bool ENCODE>
+hipError_t launch_upsweep(const K *keys, uint32_t *counts, int64_t n, int64_t block_len, int blocks, int shift,
+                          uint32_t mask, hipStream_t stream)
+{
+    const bool vec = ((uintptr_t)keys % 16) == 0;
+    return launch(LRS_KERNEL_UPSWEEP, stream, [&] {
+        if (vec)
+            upsweep_kernel<K, ENCODE, kUpsweepThreads, true>
+                <<<blocks, kUpsweepThreads, 0, stream>>>(keys, counts, n, block_len, blocks, shift, mask);
+        else
+            upsweep_kernel<K, ENCODE, kUpsweepThreads, false>
+                <<<blocks, kUpsweepThreads, 0, stream>>>(keys, counts, n, block_len, blocks, shift, mask);
+    });
+}
+
+hipError_t launch_scan(uint32_t *counts, uint32_t *rowtot, int blocks, hipStream_t stream)
+{
+    return launch(LRS_KERNEL_SCAN, stream, [&] {
+        scan_kernel<kScanThreads, kScanPerThread><<<kRadix, kScanThreads, 0, stream>>>(counts, rowtot, blocks);
+    });
+}
+
+template <typename K, bool PAIRS, int WAVES, int ITEMS, bool ENCODE, bool DECODE>
+hipError_t launch_downsweep(const K *kin, K *kout, const uint32_t *vin, uint32_t *vout, const uint32_t *counts,
+                            const uint32_t *rowtot, int64_t n, int64_t block_len, int blocks, int shift,
+                            uint32_t mask, hipStream_t stream)
+{
+    return launch(LRS_KERNEL_DOWNSWEEP, stream, [&] {
+        downsweep_kernel<K, PAIRS, WAVES, ITEMS, ENCODE, DECODE><<<blocks, WAVES * 64, 0, stream>>>(
+            kin, kout, vin, vout, counts, rowtot, n, block_len, blocks, shift, mask);
+    });
+}
+
+template <typename K, bool PAIRS, int WAVES, int ITEMS>
+hipError_t downsweep_dispatch(bool enc, bool dec, const K *kin, K *kout, const uint32_t *vin, uint32_t *vout,
+                              const uint32_t *counts, const uint32_t *rowtot, int64_t n, int64_t block_len,
+                              int blocks, int shift, uint32_t mask, hipStream_t stream)
+{
+    if constexpr (sizeof(K) == 4) {
+        if (enc && dec)
+            return launch_downsweep<K, PAIRS, WAVES, ITEMS, true, true>(kin, kout, vin, vout, counts, rowtot, n,
+                                                                         block_len, blocks, shift, mask, stream);
+        if (enc)
+            return launch_downsweep<K, PAIRS, WAVES, ITEMS, true, false>(kin, kout, vin, vout, counts, rowtot, n,
+                                                                          block_len, blocks, shift, mask, stream);
+        if (dec)
+            return launch_downsweep<K, PAIRS, WAVES, ITEMS, false, true>(kin, kout, vin, vout, counts, rowtot, n,
+                                                                          block_len, blocks, shift, mask, stream);
+    }
+    return launch_downsweep<K, PAIRS, WAVES, ITEMS, false, false>(kin, kout, vin, vout, counts, rowtot, n,
+                                                                   block_len, blocks, shift, mask, stream);
+}
+
+// The kernel whose occupancy sets the number of blocks for this key type.
+template <typename K, bool PAIRS, int WAVES, int ITEMS>
+hipError_t blocks_for(int64_t tiles, int *blocks)
+{
+    int cus = 0, per_cu = 0;
+    hipError_t err = device_cus(&cus);
+    if (err != hipSuccess) return err;
+    err = occupancy(downsweep_kernel<K, PAIRS, WAVES, ITEMS, false, false>, WAVES * 64, &per_cu);
+    if (err != hipSuccess) return err;
+    const int64_t want = std::max<int64_t>(1, (int64_t)cus * per_cu);
+    *blocks = (int)std::min<int64_t>(std::min<int64_t>(tiles, want), kMaxBlocks);
+    return hipSuccess;
+}
+
+template <typename K, bool PAIRS, int WAVES, int ITEMS>
+lrs_status run_passes(const Request &rq, const Layout &L, char *temp, hipStream_t stream)
+{
+    constexpr int TILE = WAVES * 64 * ITEMS;
+    int want_blocks = 0;
+    if (blocks_for<K, PAIRS, WAVES, ITEMS>(L.tiles, &want_blocks) != hipSuccess) return LRS_ERR_HIP;
+    const int64_t tiles_per_block = (L.tiles + want_blocks - 1) / want_blocks;
+    const int64_t block_len = tiles_per_block * TILE;
+    const int blocks = (int)((rq.n + block_len - 1) / block_len);
+
+    uint32_t *counts = (uint32_t *)(temp + L.off_counts);
+    uint32_t *rowtot = (uint32_t *)(temp + L.off_rowtot);
+    const K *kbuf_const[4] = {(const K *)rq.keys_in, (const K *)rq.keys_out, (const K *)(temp + L.off_ka),
+                              (const K *)(temp + L.off_kb)};
+    K *kbuf[4] = {nullptr, (K *)rq.keys_out, (K *)(temp + L.off_ka), (K *)(temp + L.off_kb)};
+    const uint32_t *vbuf_const[4] = {rq.vals_in, rq.vals_out, (const uint32_t *)(temp + L.off_va),
+                                     (const uint32_t *)(temp + L.off_vb)};
+    uint32_t *vbuf[4] = {nullptr, rq.vals_out, (uint32_t *)(temp + L.off_va), (uint32_t *)(temp + L.off_vb)};
+
+    const bool is_f32 = rq.kind == KIND_F32;
+    int ksrc = BUF_IN, vsrc = BUF_IN;
+    for (int p = 0; p < L.passes; ++p) {
+        const int shift = rq.begin_bit + kRadixBits * p;
+        const int width = std::min(kRadixBits, rq.end_bit - shift);
+        const uint32_t mask = (1u << width) - 1u;
+        const bool enc = is_f32 && p == 0;
+        const bool dec = is_f32 && p == L.passes - 1;
+        const int kdst = L.kplan.dst[p], vdst = L.vplan.dst[p];
+
+        hipError_t err;
+        if constexpr (sizeof(K) == 4) {
+            if (enc)
+                err = launch_upsweep<K, true>(kbuf_const[ksrc], counts, rq.n, block_len, blocks, shift, mask,
+                                              stream);
+            else
+                err = launch_upsweep<K, false>(kbuf_const[ksrc], counts, rq.n, block_len, blocks, shift, mask,
+                                               stream);
+        } else {
+            err = launch_upsweep<K, false>(kbuf_const[ksrc], counts, rq.n, block_len, blocks, shift, mask, stream);
+        }
+        if (err != hipSuccess) return LRS_ERR_HIP;
+        if (launch_scan(counts, rowtot, blocks, stream) != hipSuccess) return LRS_ERR_HIP;
+        err = downsweep_dispatch<K, PAIRS, WAVES, ITEMS>(enc, dec, kbuf_const[ksrc], kbuf[kdst],
+                                                         PAIRS ? vbuf_const[vsrc] : nullptr,
+                                                         PAIRS ? vbuf[vdst] : nullptr, counts, rowtot, rq.n,
+                                                         block_len, blocks, shift, mask, stream);
+        if (err != hipSuccess) return LRS_ERR_HIP;
+        ksrc = kdst;
+        vsrc = vdst;
+    }
+    const size_t ksz = sizeof(K);
+    if (L.kplan.copy_a_to_out) {
+        lrs_status st = copy_bytes(rq.keys_out, temp + L.off_ka, (size_t)rq.n * ksz, stream);
+        if (st != LRS_OK) return st;
+    }
+    if (PAIRS && L.vplan.copy_a_to_out) {
+        lrs_status st = copy_bytes(rq.vals_out, temp + L.off_va, (size_t)rq.n * 4, stream);
+        if (st != LRS_OK) return st;
+    }
+    return LRS_OK;
+}
+
+lrs_status sort_entry(const Request &rq, void *d_temp, size_t *temp_bytes, hipStream_t stream)
+{
+    // All checks happen before any HIP call, so they need no device.
+    if (temp_bytes == nullptr) return LRS_ERR_INVALID_ARG;
+    const int key_bits = rq.kind == KIND_U64 ? 64 : 32;
+    const size_t ksz = key_bits / 8;
+    if (rq.n < 0 || rq.n > (int64_t)0xFFFFFFFFll) return LRS_ERR_INVALID_ARG;
+    if (rq.begin_bit < 0 || rq.end_bit < rq.begin_bit || rq.end_bit > key_bits) return LRS_ERR_INVALID_ARG;
+    if (rq.n > 0) {
+        if (!rq.keys_in || !rq.keys_out) return LRS_ERR_INVALID_ARG;
+        if (((uintptr_t)rq.keys_in % ksz) || ((uintptr_t)rq.keys_out % ksz)) return LRS_ERR_INVALID_ARG;
+        if (overlap_partial(rq.keys_in, rq.keys_out, (size_t)rq.n * ksz)) return LRS_ERR_INVALID_ARG;
+    }
+    const bool pairs = rq.vals_in != nullptr || rq.vals_out != nullptr;
+    if (pairs && rq.n > 0) {
+        if (!rq.vals_in || !rq.vals_out) return LRS_ERR_INVALID_ARG;
+        if (((uintptr_t)rq.vals_in % 4) || ((uintptr_t)rq.vals_out % 4)) return LRS_ERR_INVALID_ARG;
+        if (overlap_partial(rq.vals_in, rq.vals_out, (size_t)rq.n * 4)) return LRS_ERR_INVALID_ARG;
+    }
+    Request r = rq;
+    if (!pairs || rq.n == 0) r.vals_in = nullptr, r.vals_out = nullptr;
+    const Layout L = make_layout(r);
+    if (d_temp == nullptr) {
+        *temp_bytes = L.total;
+        return LRS_OK;
+    }
+    if (*temp_bytes < L.total) return LRS_ERR_TEMP_TOO_SMALL;
+    if (r.n == 0) return LRS_OK;
+    if (L.passes == 0) {
+        lrs_status st = copy_bytes(r.keys_out, r.keys_in, (size_t)r.n * ksz, stream);
+        if (st == LRS_OK && pairs) st = copy_bytes(r.vals_out, r.vals_in, (size_t)r.n * 4, stream);
+        return st;
+    }
+    char *temp = (char *)d_temp;
+    if (r.kind == KIND_U64) {
+        if (pairs) return run_passes<uint64_t, true, kWaves64, kItems64>(r, L, temp, stream);
+        return run_passes<uint64_t, false, kWaves64, kItems64>(r, L, temp, stream);
+    }
+    if (pairs) return run_passes<uint32_t, true, kWaves32, kItems32>(r, L, temp, stream);
+    return run_passes<uint32_t, false, kWaves32, kItems32>(r, L, temp, stream);
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------- exports
+
+LRS_API lrs_status lrs_sort_keys_u32(void *d_temp, size_t *temp_bytes, const uint32_t *d_keys_in,
+                                     uint32_t *d_keys_out, int64_t n, int begin_bit, int end_bit,
+                                     hipStream_t stream)
+{
+    return sort_entry({KIND_U32, d_keys_in, d_keys_out, nullptr, nullptr, n, begin_bit, end_bit}, d_temp,
+                      temp_bytes, stream);
+}
+
+LRS_API lrs_status lrs_sort_keys_u64(void *d_temp, size_t *temp_bytes, const uint64_t *d_keys_in,
+                                     uint64_t *d_keys_out, int64_t n, int begin_bit, int end_bit,
+                                     hipStream_t stream)
+{
+    return sort_entry({KIND_U64, d_keys_in, d_keys_out, nullptr, nullptr, n, begin_bit, end_bit}, d_temp,
+                      temp_bytes, stream);
+}
+
+LRS_API lrs_status lrs_sort_keys_f32(void *d_temp, size_t *temp_bytes, const float *d_keys_in, float *d_keys_out,
+                                     int64_t n, int begin_bit, int end_bit, hipStream_t stream)
+{
+    return sort_entry({KIND_F32, d_keys_in, d_keys_out, nullptr, nullptr, n, begin_bit, end_bit}, d_temp,
+                      temp_bytes, stream);
+}
+
+LRS_API lrs_status lrs_sort_pairs_u32(void *d_temp, size_t *temp_bytes, const uint32_t *d_keys_in,
+                                      const uint32_t *d_values_in, uint32_t *d_keys_out, uint32_t *d_values_out,
+                                      int64_t n, int begin_bit, int end_bit, hipStream_t stream)
+{
+    if (n > 0 && (!d_values_in || !d_values_out)) return LRS_ERR_INVALID_ARG;
+    return sort_entry({KIND_U32, d_keys_in, d_keys_out, d_values_in, d_values_out, n, begin_bit, end_bit}, d_temp,
+                      temp_bytes, stream);
+}
+
+LRS_API lrs_status lrs_sort_pairs_u64(void *d_temp, size_t *temp_bytes, const uint64_t *d_keys_in,
+                                      const uint32_t *d_values_in, uint64_t *d_keys_out, uint32_t *d_values_out,
+                                      int64_t n, int begin_bit, int end_bit, hipStream_t stream)
+{
+    if (n > 0 && (!d_values_in || !d_values_out)) return LRS_ERR_INVALID_ARG;
+    return sort_entry({KIND_U64, d_keys_in, d_keys_out, d_values_in, d_values_out, n, begin_bit, end_bit}, d_temp,
+                      temp_bytes, stream);
+}
+
+LRS_API lrs_status lrs_sort_pairs_f32(void *d_temp, size_t *temp_bytes, const float *d_keys_in,
+                                      const uint32_t *d_values_in, float *d_keys_out, uint32_t *d_values_out,
+                                      int64_t n, int begin_bit, int end_bit, hipStream_t stream)
+{
+    if (n > 0 && (!d_values_in || !d_values_out)) return LRS_ERR_INVALID_ARG;
+    return sort_entry({KIND_F32, d_keys_in, d_keys_out, d_values_in, d_values_out, n, begin_bit, end_bit}, d_temp,
+                      temp_bytes, stream);
+}
+
+LRS_API const char *lrs_status_string(lrs_status status)
+{
+    switch (status) {
+    case LRS_OK: return "LRS_OK: success";
+    case LRS_ERR_INVALID_ARG: return "LRS_ERR_INVALID_ARG: invalid argument";
+    case LRS_ERR_TEMP_TOO_SMALL: return "LRS_ERR_TEMP_TOO_SMALL: temp storage smaller than required";
+    case LRS_ERR_HIP: return "LRS_ERR_HIP: a HIP call or kernel launch failed";
+    }
+    return "unknown lrs_status";
+}
+
+LRS_API lrs_status lrs_device_copy(void *d_dst, const void *d_src, size_t bytes, hipStream_t stream)
+{
+    if (bytes > 0 && (!d_dst || !d_src)) return LRS_ERR_INVALID_ARG;
+    return copy_bytes(d_dst, d_src, bytes, stream);
+}
+
+LRS_API lrs_status lrs_prof_start(int capacity)
+{
+    if (capacity <= 0) return LRS_ERR_INVALID_ARG;
+    lrs_prof_release();
+    g_prof.ev.assign(2 * (size_t)capacity, nullptr);
+    g_prof.kind.assign(capacity, 0);
+    for (auto &e : g_prof.ev) {
+        if (hipEventCreate(&e) != hipSuccess) {
+            e = nullptr;
+            lrs_prof_release();
+            return LRS_ERR_HIP;
+        }
+    }
+    g_prof.cap = capacity;
+    g_prof.count = 0;
+    g_prof.on = true;
+    return LRS_OK;
+}
+
+LRS_API lrs_status lrs_prof_stop(void)
+{
+    g_prof.on = false;
+    return LRS_OK;
+}
+
+LRS_API int lrs_prof_count(void) { return g_prof.count; }
+
+LRS_API lrs_status lrs_prof_read(int i, int *kind, float *ms)
+{
+    if (i < 0 || i >= g_prof.count || !kind || !ms) return LRS_ERR_INVALID_ARG;
+    if (hipEventSynchronize(g_prof.ev[2 * i + 1]) != hipSuccess) return LRS_ERR_HIP;
+    float t = 0.f;
+    if (hipEventElapsedTime(&t, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]) != hipSuccess) return LRS_ERR_HIP;
+    *kind = g_prof.kind[i];
+    *ms = t;
+    return LRS_OK;
+}
+
+LRS_API lrs_status lrs_prof_release(void)
+{
+    for (auto &e : g_prof.ev)
+        if (e) (void)hipEventDestroy(e);
+    g_prof.ev.clear();
+    g_prof.kind.clear();
+    g_prof.on = false;
+    g_prof.cap = 0;
+    g_prof.count = 0;
+    return LRS_OK;
+}

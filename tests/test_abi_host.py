@@ -1,0 +1,139 @@
+"""Host-only checks of the C ABI (no GPU): the library loads, exports every
+function the headers declare, answers temp-size queries and rejects bad
+arguments before touching a device."""
+from __future__ import annotations
+
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import sorting_lsd_radix_sort_amd as lrs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# fake, well-aligned device addresses: queries and argument errors never dereference them
+A, B, C, D, T = 1 << 40, 2 << 40, 3 << 40, 4 << 40, 5 << 40
+
+
+def header_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names.update(re.findall(r"\b(lrs_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
+
+
+def test_library_loads_and_exports_header_symbols():
+    lib = lrs.load_library()
+    declared = header_functions()
+    assert "lrs_sort_pairs_f32" in declared and len(declared) >= 12
+    for name in declared:
+        assert hasattr(lib, name), "missing export " + name
+    assert set(declared) == set(lrs.EXPORTED)
+
+
+def test_status_strings():
+    for st in (lrs.LRS_OK, lrs.LRS_ERR_INVALID_ARG, lrs.LRS_ERR_TEMP_TOO_SMALL, lrs.LRS_ERR_HIP):
+        assert lrs.status_string(st).startswith("LRS_")
+    assert "unknown" in lrs.status_string(99)
+
+
+def q_keys(sfx, n, b, e, kin=A, kout=B):
+    return getattr(lrs, "lrs_sort_keys_" + sfx)(None, 0, kin, kout, n, b, e)
+
+
+def q_pairs(sfx, n, b, e, kin=A, vin=C, kout=B, vout=D):
+    return getattr(lrs, "lrs_sort_pairs_" + sfx)(None, 0, kin, vin, kout, vout, n, b, e)
+
+
+@pytest.mark.parametrize("sfx,ksz,bits", [("u32", 4, 32), ("f32", 4, 32), ("u64", 8, 64)])
+def test_temp_query_sizes(sfx, ksz, bits):
+    n = 100_000_000
+    # out-of-place, >= 2 passes: one alternate key buffer plus a small count matrix
+    t = q_keys(sfx, n, 0, bits)
+    assert ksz * n <= t <= ksz * n + 8 * 2**20
+    # one pass out-of-place needs no alternate buffer
+    assert q_keys(sfx, n, 0, 8) <= 8 * 2**20
+    # in-place with an even pass count: still one alternate buffer
+    assert q_keys(sfx, n, 0, 16, kin=A, kout=A) == q_keys(sfx, n, 0, 16)
+    # in-place with an odd pass count (>= 3): two alternate buffers
+    t3 = q_keys(sfx, n, 0, 24, kin=A, kout=A)
+    assert 2 * ksz * n <= t3 <= 2 * ksz * n + 8 * 2**20
+    # in-place single pass: one alternate buffer (result copied back)
+    t1 = q_keys(sfx, n, 0, 8, kin=A, kout=A)
+    assert ksz * n <= t1 <= ksz * n + 8 * 2**20
+    # pairs add an alternate value buffer
+    tp = q_pairs(sfx, n, 0, bits)
+    assert (ksz + 4) * n <= tp <= (ksz + 4) * n + 8 * 2**20
+    # the count matrix is bounded, so temp grows linearly with n
+    assert q_keys(sfx, 2 * n, 0, bits) - 2 * t <= 8 * 2**20
+
+
+def test_temp_query_small_and_empty():
+    assert q_keys("u32", 0, 0, 32) > 0            # always a usable non-zero size
+    assert q_keys("u32", 1, 0, 32) < 64 * 1024
+    assert q_keys("u32", 5, 3, 3) < 64 * 1024     # empty bit range: plain copy
+
+
+@pytest.mark.parametrize("sfx,bits", [("u32", 32), ("f32", 32), ("u64", 64)])
+def test_invalid_bit_ranges(sfx, bits):
+    for b, e in [(-1, 8), (9, 8), (0, bits + 1), (bits + 1, bits + 1)]:
+        with pytest.raises(lrs.LrsError) as ei:
+            q_keys(sfx, 10, b, e)
+        assert ei.value.status == lrs.LRS_ERR_INVALID_ARG
+    q_keys(sfx, 10, bits, bits)  # empty range at the top is valid
+
+
+def test_invalid_sizes_and_pointers():
+    for n in (-1, 2**32, 2**40):
+        with pytest.raises(lrs.LrsError) as ei:
+            q_keys("u32", n, 0, 32)
+        assert ei.value.status == lrs.LRS_ERR_INVALID_ARG
+    q_keys("u32", 2**32 - 1, 0, 32)  # the largest n is accepted
+    bad = [dict(kin=0), dict(kout=0), dict(kin=A + 2), dict(kout=B + 4 * 3 + 1),
+           dict(kin=A, kout=A + 4)]   # partial overlap of input and output
+    for kw in bad:
+        with pytest.raises(lrs.LrsError) as ei:
+            q_keys("u32", 1000, 0, 32, **kw)
+        assert ei.value.status == lrs.LRS_ERR_INVALID_ARG, kw
+    with pytest.raises(lrs.LrsError):
+        q_keys("u64", 10, 0, 64, kin=A + 4)  # uint64 keys need 8-byte alignment
+    for kw in (dict(vin=0), dict(vout=0), dict(vin=C + 1), dict(vin=C, vout=C + 8)):
+        with pytest.raises(lrs.LrsError) as ei:
+            q_pairs("u32", 1000, 0, 32, **kw)
+        assert ei.value.status == lrs.LRS_ERR_INVALID_ARG, kw
+    # NULL pointers are fine when there is nothing to sort
+    assert q_keys("u32", 0, 0, 32, kin=0, kout=0) > 0
+
+
+def test_temp_too_small_and_empty_input_touch_nothing():
+    need = q_keys("u32", 1_000_000, 0, 32)
+    with pytest.raises(lrs.LrsError) as ei:
+        lrs.lrs_sort_keys_u32(T, need - 1, A, B, 1_000_000, 0, 32, 0)
+    assert ei.value.status == lrs.LRS_ERR_TEMP_TOO_SMALL
+    with pytest.raises(lrs.LrsError) as ei:
+        lrs.lrs_sort_pairs_f32(T, 16, A, C, B, D, 1_000_000, 0, 32, 0)
+    assert ei.value.status == lrs.LRS_ERR_TEMP_TOO_SMALL
+    # n == 0 returns before any device work
+    need0 = q_keys("u32", 0, 0, 32)
+    assert lrs.lrs_sort_keys_u32(T, need0, A, B, 0, 0, 32, 0) == need0
+
+
+def test_null_temp_bytes_pointer():
+    lib = lrs.load_library()
+    assert lib.lrs_sort_keys_u32(None, None, A, B, 10, 0, 32, None) == lrs.LRS_ERR_INVALID_ARG
+
+
+def test_device_copy_and_prof_argument_checks():
+    lib = lrs.load_library()
+    assert lib.lrs_device_copy(None, ctypes.c_void_p(A), 16, None) == lrs.LRS_ERR_INVALID_ARG
+    assert lib.lrs_device_copy(None, None, 0, None) == lrs.LRS_OK
+    assert lib.lrs_prof_start(0) == lrs.LRS_ERR_INVALID_ARG
+    assert lib.lrs_prof_count() == 0
+    k, ms = ctypes.c_int(), ctypes.c_float()
+    assert lib.lrs_prof_read(0, ctypes.byref(k), ctypes.byref(ms)) == lrs.LRS_ERR_INVALID_ARG
+    assert lib.lrs_prof_release() == lrs.LRS_OK

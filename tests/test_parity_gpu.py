@@ -1,0 +1,209 @@
+"""Parity of the HIP sort (through the C ABI) with the CPU oracle, on cuda:0.
+
+- Element-by-element, bit-exact comparison with the oracle on seeded inputs of
+  every key type, with and without payload, over full and partial bit ranges,
+  at sizes from empty through single tiles, ragged tails and multi-tile blocks.
+- At the workloads' full sizes, in the launch configuration the benchmark
+  times: properties that pin the unique correct output exactly.  For a pair
+  sort whose payload is the original index, "payload is a permutation of
+  0..n-1, each output key is the input key its payload names, keys are ordered,
+  equal keys have increasing payload" holds only for the stable sort itself.
+  For a keys-only sort whose bit range covers every key bit, the output must
+  equal numpy's sort of the input.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import checks
+import oracle
+import sorting_lsd_radix_sort_amd as lrs
+from gpu_util import announce, gpu_sort, to_dev, to_host
+from sorting_lsd_radix_sort_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+TILE = 4096
+SMALL_SIZES = [0, 1, 2, 3, 63, 64, 65, 255, 256, 257, TILE - 1, TILE, TILE + 1, 3 * TILE + 17, 65_536]
+RANGES = {"u32": [(0, 32), (0, 20), (8, 16), (3, 17), (31, 32), (24, 32), (5, 5)],
+          "f32": [(0, 32), (0, 20), (16, 32), (31, 32)],
+          "u64": [(0, 64), (0, 40), (32, 64), (5, 61), (63, 64)]}
+
+
+def _compare(keys, vals, b, e, **kw):
+    got_k, got_v = gpu_sort(keys, vals, b, e, **kw)
+    if vals is None:
+        want_k = oracle.sort_keys(keys, b, e)
+        i = checks.first_mismatch(got_k, want_k)
+        assert i < 0, "key mismatch at %d (n=%d, bits [%d,%d))" % (i, keys.size, b, e)
+    else:
+        want_k, want_v = oracle.sort_pairs(keys, vals, b, e)
+        i = checks.first_mismatch(got_k, want_k)
+        assert i < 0, "key mismatch at %d (n=%d, bits [%d,%d))" % (i, keys.size, b, e)
+        j = checks.first_mismatch(got_v, want_v)
+        assert j < 0, "value mismatch at %d (n=%d, bits [%d,%d))" % (j, keys.size, b, e)
+
+
+# ------------------------------------------------------------ small sizes, oracle
+
+@pytest.mark.parametrize("key_type", ["u32", "f32", "u64"])
+@pytest.mark.parametrize("pairs", [False, True])
+def test_small_sizes_all_ranges(key_type, pairs):
+    for n in SMALL_SIZES:
+        for dist in ("uniform", "dup"):
+            keys = inputs.random_keys(key_type, n, 1000 + n, dist)
+            vals = np.arange(n, dtype=np.uint32) if pairs else None
+            for b, e in RANGES[key_type]:
+                announce("small %s pairs=%s n=%d dist=%s bits=[%d,%d)" % (key_type, pairs, n, dist, b, e))
+                _compare(keys, vals, b, e)
+
+
+@pytest.mark.parametrize("key_type,dist", [("u32", "and3"), ("u64", "and3"), ("f32", "f32mix"),
+                                           ("u32", "dup"), ("f32", "uniform")])
+def test_skewed_and_special_values(key_type, dist):
+    n = 5 * TILE + 1234
+    keys = inputs.random_keys(key_type, n, 77, dist)
+    for pairs in (False, True):
+        vals = np.random.default_rng(5).permutation(n).astype(np.uint32) if pairs else None
+        for b, e in RANGES[key_type][:3]:
+            announce("skew %s %s pairs=%s bits=[%d,%d)" % (key_type, dist, pairs, b, e))
+            _compare(keys, vals, b, e)
+
+
+# ------------------------------------------------- workloads at reduced sizes, oracle
+
+REDUCED = {"c1_u32_keys_64k": None, "c2_u32_keys_1e8": 4_194_304 + 1237,
+           "c3a_u32_pairs_and3": 2_097_152 + 999, "c3b_u32_pairs_equal": 2_097_152 + 5,
+           "c3b0_u32_pairs_zero": 1_000_003, "c4_f32_pairs_normal": 2_097_152 + 77,
+           "c5a_u64_pairs": 1_048_576 + 4095, "c5b_u32_pairs_20bit": 2_097_152 + 1,
+           "c5b_u32_keys_20bit": 2_097_152 + 4097}
+
+
+@pytest.mark.parametrize("name", list(REDUCED))
+def test_workloads_reduced_vs_oracle(name):
+    cfg, keys, vals = inputs.draw(name, REDUCED[name])
+    announce("reduced %s n=%d" % (name, keys.size))
+    _compare(keys, vals, cfg.begin_bit, cfg.end_bit)
+
+
+@pytest.mark.parametrize("key_type,n,pairs", [("u32", 12_500_003, False), ("f32", 9_000_001, True),
+                                              ("u64", 6_000_011, True)])
+def test_multi_tile_blocks_vs_oracle(key_type, n, pairs):
+    """Large enough that each workgroup walks several tiles of its block."""
+    keys = inputs.random_keys(key_type, n, 31, "uniform" if key_type != "f32" else "f32mix")
+    vals = np.arange(n, dtype=np.uint32) if pairs else None
+    bits = 64 if key_type == "u64" else 32
+    announce("multi-tile %s n=%d pairs=%s" % (key_type, n, pairs))
+    _compare(keys, vals, 0, bits)
+
+
+# ------------------------------------------------------------------ in-place use
+
+@pytest.mark.parametrize("key_type", ["u32", "f32", "u64"])
+def test_in_place(key_type):
+    n = 3 * TILE + 101
+    keys = inputs.random_keys(key_type, n, 9, "dup" if key_type != "f32" else "f32mix")
+    vals = np.random.default_rng(3).permutation(n).astype(np.uint32)
+    bits = 64 if key_type == "u64" else 32
+    # 1, 2, 3 and 4 passes (odd pass counts need the second alternate buffer)
+    for b, e in [(0, 8), (0, 16), (0, 24), (bits - 32, bits), (4, 9)]:
+        for ipk, ipv in [(True, False), (False, True), (True, True)]:
+            announce("in-place %s bits=[%d,%d) keys=%s vals=%s" % (key_type, b, e, ipk, ipv))
+            _compare(keys, vals, b, e, in_place_keys=ipk, in_place_vals=ipv)
+        announce("in-place keys-only %s bits=[%d,%d)" % (key_type, b, e))
+        _compare(keys, None, b, e, in_place_keys=True)
+
+
+def test_input_not_modified_and_deterministic():
+    import torch
+    cfg, keys, vals = inputs.draw("c4_f32_pairs_normal", 3_000_017)
+    announce("input-unchanged/determinism n=%d" % keys.size)
+    kin, vin = to_dev(keys), to_dev(vals)
+    outs = []
+    for _ in range(2):
+        ko, vo = lrs.sort_pairs(kin, vin)
+        torch.cuda.synchronize()
+        outs.append((to_host(ko), to_host(vo)))
+    assert np.array_equal(to_host(kin).view(np.uint32), keys.view(np.uint32))
+    assert np.array_equal(to_host(vin), vals)
+    assert np.array_equal(outs[0][0].view(np.uint32), outs[1][0].view(np.uint32))
+    assert np.array_equal(outs[0][1], outs[1][1])
+
+
+def test_side_stream_and_misaligned_input():
+    """Sorts on a non-default stream, from a key array that is not 16-byte aligned."""
+    import torch
+    n = 200_003
+    keys = inputs.random_keys("u32", n + 1, 4)
+    announce("side stream, misaligned input n=%d" % n)
+    base = to_dev(keys)
+    kin = base[1:]            # 4-byte aligned, not 16-byte aligned
+    assert kin.data_ptr() % 16 != 0
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        out = lrs.sort_keys(kin, stream=s)
+    s.synchronize()
+    assert np.array_equal(to_host(out), oracle.sort_keys(keys[1:]))
+
+
+def test_temp_too_small_on_device():
+    import torch
+    keys = to_dev(inputs.random_keys("u32", 10_000, 1))
+    out = torch.empty_like(keys)
+    need = lrs.lrs_sort_keys_u32(None, 0, keys, out, keys.numel(), 0, 32)
+    temp = torch.empty(need, dtype=torch.uint8, device="cuda:0")
+    announce("temp too small")
+    with pytest.raises(lrs.LrsError) as ei:
+        lrs.lrs_sort_keys_u32(temp, need - 256, keys, out, keys.numel(), 0, 32)
+    assert ei.value.status == lrs.LRS_ERR_TEMP_TOO_SMALL
+
+
+def test_device_copy():
+    import torch
+    a = to_dev(inputs.random_keys("u32", 1_000_003, 8))
+    b = torch.empty_like(a)
+    announce("device copy")
+    lrs.lrs_device_copy(b, a, a.numel() * 4)
+    lrs.lrs_device_copy(b[1:], a[1:], 4 * 1000)   # unaligned start
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_profiling_records_every_launch():
+    import torch
+    keys = to_dev(inputs.random_keys("u64", 300_000, 2))
+    announce("profiling hooks")
+    lrs.lrs_prof_start(64)
+    try:
+        lrs.sort_keys(keys)           # 8 passes x 3 kernels
+        torch.cuda.synchronize()
+        lrs.lrs_prof_stop()
+        recs = [lrs.lrs_prof_read(i) for i in range(lrs.lrs_prof_count())]
+    finally:
+        lrs.lrs_prof_release()
+    assert [k for k, _ in recs] == [0, 1, 2] * 8
+    assert all(ms > 0 for _, ms in recs)
+
+
+# --------------------------------------------------------- full sizes, properties
+
+FULL = ["c1_u32_keys_64k", "c2_u32_keys_1e8", "c3a_u32_pairs_and3", "c3b_u32_pairs_equal",
+        "c3b0_u32_pairs_zero", "c4_f32_pairs_normal", "c5a_u64_pairs", "c5b_u32_pairs_20bit",
+        "c5b_u32_keys_20bit"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_workloads_full_size(name):
+    cfg, keys, vals = inputs.draw(name)
+    announce("full %s n=%d" % (name, keys.size))
+    got_k, got_v = gpu_sort(keys, vals, cfg.begin_bit, cfg.end_bit)
+    if vals is not None:
+        checks.check_pairs(keys, got_k, got_v, cfg.begin_bit, cfg.end_bit)
+        if cfg.dist == "equal":
+            assert np.array_equal(got_v, vals) and np.array_equal(got_k, keys)
+    else:
+        # every key bit lies in the sorted range, so the output is numpy's sort
+        assert int(checks.raw_bits(keys).max()) < (1 << cfg.end_bit) and cfg.begin_bit == 0
+        i = checks.first_mismatch(got_k, np.sort(keys))
+        assert i < 0, "mismatch with np.sort at %d" % i
