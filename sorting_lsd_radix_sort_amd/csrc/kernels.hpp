@@ -40,6 +40,8 @@ constexpr int kRadixBits = 8;
 constexpr int kRadix = 1 << kRadixBits;
 constexpr int kWave = 64;
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 // ------------------------------------------------------------------ key codes
 
 // Float32 bit pattern -> order-preserving unsigned word (kwkr.cn essay,
@@ -63,27 +65,66 @@ __device__ __forceinline__ uint32_t digit_of(K k, int shift, uint32_t mask)
 
 // --------------------------------------------------------------- wave helpers
 
+// All-ones if bit b of d is set, else zero.  Written as the instruction itself
+// so the compiler keeps one v_bfe_i32 per bit and derives the ballot from its
+// result instead of re-testing d with an extra shift.
+template <int B>
+__device__ __forceinline__ uint32_t bit_mask(uint32_t d)
+{
+    uint32_t t;
+    asm("v_bfe_i32 %0, %1, %2, 1" : "=v"(t) : "v"(d), "i"(B));
+    return t;
+}
+
 // Lanes of the wave whose 8-bit digit equals this lane's: for each digit bit,
-// keep the lanes whose ballot bit agrees with ours.  All 64 lanes must be
+// keep the lanes whose ballot bit agrees with ours (the 64-lane form of the
+// ballot / popcount / lanes-below rank of the warp partition walked through on
+// the blog.csdn.net page about the qsort_warp sample).  All 64 lanes must be
 // active.  v_bitop3 0x90 computes m & ~(ballot ^ t): with t all-ones when our
-// bit is set it keeps the ballot, otherwise its complement.
+// bit is set it keeps the ballot, otherwise its complement.  Four VALU
+// instructions per digit bit.
+template <int B = 0>
+__device__ __forceinline__ void match_bits(uint32_t d, uint32_t &lo, uint32_t &hi)
+{
+    if constexpr (B < kRadixBits) {
+        const uint32_t t = bit_mask<B>(d);
+        const uint64_t bal = __ballot(t != 0u);
+        lo = __builtin_amdgcn_bitop3_b32(lo, (uint32_t)bal, t, 0x90);
+        hi = __builtin_amdgcn_bitop3_b32(hi, (uint32_t)(bal >> 32), t, 0x90);
+        match_bits<B + 1>(d, lo, hi);
+    }
+}
+
 __device__ __forceinline__ void match_digit(uint32_t d, uint32_t &lo, uint32_t &hi)
 {
     lo = 0xFFFFFFFFu;
     hi = 0xFFFFFFFFu;
-#pragma unroll
-    for (int b = 0; b < kRadixBits; ++b) {
-        const uint32_t t = (uint32_t)((int32_t)(d << (31 - b)) >> 31);
-        const uint64_t bal = __ballot(t != 0u);
-        lo = __builtin_amdgcn_bitop3_b32(lo, (uint32_t)bal, t, 0x90);
-        hi = __builtin_amdgcn_bitop3_b32(hi, (uint32_t)(bal >> 32), t, 0x90);
-    }
+    match_bits<0>(d, lo, hi);
 }
 
 // Number of set bits of (hi:lo) in lanes below this one.
 __device__ __forceinline__ uint32_t lanes_below(uint32_t lo, uint32_t hi)
 {
     return __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u));
+}
+
+// Inclusive prefix sum over the 64 lanes with DPP moves (no LDS): shifts of
+// 1, 2, 4 and 8 lanes inside each row of 16, then row 0's and rows 0-1's
+// last lanes broadcast into the rows above.  All lanes must be active.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x)
+{
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return x;
+}
+
+__device__ __forceinline__ uint32_t wave_broadcast_last(uint32_t x)
+{
+    return __builtin_amdgcn_readlane(x, kWave - 1);
 }
 
 // Exclusive prefix sum of one value per thread over the whole workgroup.
@@ -94,12 +135,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *s
     constexpr int WAVES = THREADS / kWave;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    uint32_t x = v;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const uint32_t y = __shfl_up(x, off, kWave);
-        if (lane >= off) x += y;
-    }
+    const uint32_t x = wave_inclusive_scan(v);
     if (lane == kWave - 1) s_tmp[wave] = x;
     __syncthreads();
     uint32_t before = 0, all = 0;
@@ -114,10 +150,20 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *s
     return before + x - v;
 }
 
+// Exclusive prefix sum over the 256 digits, run by one wave: lane l owns
+// digits 4l..4l+3 (one 16-byte vector).  Returns the lane's four exclusive
+// prefixes; `lane_total` is the sum of its four inputs.
+__device__ __forceinline__ uint4 wave_scan_digits(uint4 c)
+{
+    const uint32_t p1 = c.x, p2 = p1 + c.y, p3 = p2 + c.z, sum = p3 + c.w;
+    const uint32_t base = wave_inclusive_scan(sum) - sum;
+    return make_uint4(base, base + p1, base + p2, base + p3);
+}
+
 // -------------------------------------------------------------------- upsweep
 
 // Counts the digits of block b = keys [b * block_len, min(n, (b+1) * block_len)).
-// Each wave adds into its own 256-bin LDS histogram, so atomics only contend
+// Each wave adds into its own LDS sub-histograms, so atomics only contend
 // within a wave (the kwkr.cn essay, section 3.2, and the quant67.com survey,
 // section 8.1: per-block and per-warp counting instead of global atomics).
 // VEC loads 16 bytes per lane when the key array is 16-byte aligned.
@@ -127,10 +173,15 @@ __global__ __launch_bounds__(THREADS) void upsweep_kernel(
     int num_blocks, int shift, uint32_t mask)
 {
     constexpr int WAVES = THREADS / kWave;
-    __shared__ uint32_t hist[WAVES][kRadix];
+    // COPIES sub-histograms per wave (lane % COPIES picks one), padded by one
+    // word so that equal digits in different copies fall in different banks:
+    // skewed digits then serialize at most 64/COPIES lanes per atomic.
+    constexpr int COPIES = 4;
+    constexpr int STRIDE = kRadix + 1;
+    __shared__ uint32_t hist[WAVES * COPIES][STRIDE];
     const int tid = threadIdx.x;
-    uint32_t *h = hist[tid / kWave];
-    for (int i = tid; i < WAVES * kRadix; i += THREADS) (&hist[0][0])[i] = 0u;
+    uint32_t *h = hist[(tid / kWave) * COPIES + (tid % COPIES)];
+    for (int i = tid; i < WAVES * COPIES * STRIDE; i += THREADS) (&hist[0][0])[i] = 0u;
     __syncthreads();
 
     const int64_t begin = (int64_t)blockIdx.x * block_len;
@@ -155,7 +206,10 @@ __global__ __launch_bounds__(THREADS) void upsweep_kernel(
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) {
                 const int64_t i = base + (int64_t)u * THREADS + tid;
-                if (i < vend) v[u] = vk[i];
+                if (i < vend) {
+                    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(&vk[i]));
+                    v[u] = make_uint4(t.x, t.y, t.z, t.w);
+                }
             }
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) {
@@ -173,13 +227,13 @@ __global__ __launch_bounds__(THREADS) void upsweep_kernel(
         }
         scalar_from = vend * PER;
     }
-    for (int64_t i = scalar_from + tid; i < end; i += THREADS) count_key(keys[i]);
+    for (int64_t i = scalar_from + tid; i < end; i += THREADS) count_key(__builtin_nontemporal_load(&keys[i]));
     __syncthreads();
 
     for (int d = tid; d < kRadix; d += THREADS) {
         uint32_t s = 0;
 #pragma unroll
-        for (int w = 0; w < WAVES; ++w) s += hist[w][d];
+        for (int w = 0; w < WAVES * COPIES; ++w) s += hist[w][d];
         counts[(int64_t)d * num_blocks + blockIdx.x] = s;
     }
 }
@@ -219,26 +273,62 @@ __global__ __launch_bounds__(THREADS) void scan_kernel(uint32_t *__restrict__ co
 
 // ------------------------------------------------------------------ downsweep
 
-template <typename K, int WAVES, int ITEMS>
+template <typename K, bool PAIRS, int WAVES, int ITEMS>
 struct DownsweepSmem {
     static constexpr int kThreads = WAVES * kWave;
     static constexpr int kTile = kThreads * ITEMS;
-    union {
-        K keys[kTile];
-        uint32_t vals[kTile];
-    } x;
-    uint32_t wave_count[WAVES][kRadix];  // per-wave digit counters, then offsets
-    uint32_t out_base[kRadix];           // global index of tile slot 0 of digit d
-    uint32_t run[kRadix];                // next global index of digit d in this block
-    uint32_t scan_tmp[WAVES];
+    K keys[kTile];                                      // tile in digit order
+    uint32_t vals[PAIRS ? kTile : 1];                   // payload in digit order
+    alignas(16) uint32_t wave_count[WAVES][kRadix];     // per-wave digit counts, then slot bases
+    alignas(16) uint32_t out_base[kRadix];              // global index of tile slot 0 of digit d
+    alignas(16) uint32_t run[kRadix];                   // next global index of digit d in this block
+    uint32_t sink[WAVES][kWave];                        // stores of non-leader lanes land here
 };
+
+// Issues the loads of one tile's keys for this lane: item i is key
+// first + i*64 of the tile.  The loads are non-temporal: each key is read once
+// per kernel, and keeping the stream out of L2 leaves it to the scattered
+// output lines that are still being filled.  A full tile loads from the tile base plus a
+// per-item immediate offset; in the short last tile, indices past the last
+// valid key are clamped to it, so every load stays inside the input (finish_tile
+// overwrites those slots).  Nothing here waits for the loads.
+template <typename K, int ITEMS>
+__device__ __forceinline__ void issue_tile_loads(K (&k)[ITEMS], const K *__restrict__ tile, int first, int valid)
+{
+    if (valid >= ITEMS * kWave * (int)(blockDim.x / kWave)) {
+#pragma unroll
+        for (int i = 0; i < ITEMS; ++i)
+            k[i] = __builtin_nontemporal_load(&tile[(uint32_t)first + (uint32_t)(i * kWave)]);
+    } else {
+        const uint32_t last = (uint32_t)(valid - 1);
+#pragma unroll
+        for (int i = 0; i < ITEMS; ++i)
+            k[i] = __builtin_nontemporal_load(&tile[min((uint32_t)(first + i * kWave), last)]);
+    }
+}
+
+// Applies the float encoding (first pass) and gives slots past `valid`
+// all-ones, i.e. the largest digit of any pass, so they rank after every real
+// key of the tile.
+template <typename K, bool ENCODE, int ITEMS>
+__device__ __forceinline__ void finish_tile(K (&k)[ITEMS], int first, int valid, bool full)
+{
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) {
+        if constexpr (ENCODE) k[i] = (K)encode_f32((uint32_t)k[i]);
+    }
+    if (!full) {
+#pragma unroll
+        for (int i = 0; i < ITEMS; ++i)
+            if (first + i * kWave >= valid) k[i] = ~(K)0;
+    }
+}
 
 // Stable rank + scatter of block b's tiles for one digit.  Tile layout: wave w
 // owns keys [w*64*ITEMS, (w+1)*64*ITEMS) of the tile, item i of lane l is key
 // w*64*ITEMS + i*64 + l, so each load instruction reads 64 consecutive keys and
-// (item, lane) order is input order.  Slots past the end of the input (only in
-// the last tile) take digit 255 and rank after every real key, so they land in
-// the tile's last slots and are never written.
+// (item, lane) order is input order.  The next tile's keys are loaded into
+// registers while the current tile is ranked and written.
 template <typename K, bool PAIRS, int WAVES, int ITEMS, bool ENCODE, bool DECODE>
 __global__ __launch_bounds__(WAVES * kWave) void downsweep_kernel(
     const K *__restrict__ keys_in, K *__restrict__ keys_out, const uint32_t *__restrict__ vals_in,
@@ -246,11 +336,12 @@ __global__ __launch_bounds__(WAVES * kWave) void downsweep_kernel(
     const uint32_t *__restrict__ row_total, int64_t n, int64_t block_len, int num_blocks, int shift,
     uint32_t mask)
 {
-    using Smem = DownsweepSmem<K, WAVES, ITEMS>;
+    using Smem = DownsweepSmem<K, PAIRS, WAVES, ITEMS>;
     constexpr int THREADS = Smem::kThreads;
     constexpr int TILE = Smem::kTile;
     constexpr int WAVE_KEYS = kWave * ITEMS;
     static_assert(THREADS >= kRadix, "one thread per digit is assumed");
+    static_assert(TILE <= 65536, "ranks are packed in 16 bits");
     __shared__ Smem s;
 
     const int tid = threadIdx.x;
@@ -259,133 +350,152 @@ __global__ __launch_bounds__(WAVES * kWave) void downsweep_kernel(
     const int blk = blockIdx.x;
     const int64_t blk_begin = (int64_t)blk * block_len;
     const int64_t blk_end = blk_begin + block_len < n ? blk_begin + block_len : n;
+    const int first = wave * WAVE_KEYS + lane;
+    const uint32_t n32 = (uint32_t)n;
 
-    {   // digit starts, then this block's first output index per digit
-        uint32_t total;
-        const uint32_t t = tid < kRadix ? row_total[tid] : 0u;
-        const uint32_t start = block_exclusive_scan<THREADS>(t, s.scan_tmp, total);
-        if (tid < kRadix) s.run[tid] = start + counts[(int64_t)tid * num_blocks + blk];
+    if (wave == 0) {
+        // digit starts (exclusive prefix of the row totals), plus this block's
+        // exclusive prefix within each digit's row
+        const uint4 tot = reinterpret_cast<const uint4 *>(row_total)[lane];
+        const uint4 start = wave_scan_digits(tot);
+        const int d0 = 4 * lane;
+        uint4 r;
+        r.x = start.x + counts[(int64_t)(d0 + 0) * num_blocks + blk];
+        r.y = start.y + counts[(int64_t)(d0 + 1) * num_blocks + blk];
+        r.z = start.z + counts[(int64_t)(d0 + 2) * num_blocks + blk];
+        r.w = start.w + counts[(int64_t)(d0 + 3) * num_blocks + blk];
+        reinterpret_cast<uint4 *>(s.run)[lane] = r;
+    }
+
+    K cur[ITEMS];
+    {
+        const int valid0 = blk_end - blk_begin < TILE ? (int)(blk_end - blk_begin) : TILE;
+        issue_tile_loads<K, ITEMS>(cur, keys_in + blk_begin, first, valid0);
     }
 
     for (int64_t tile_begin = blk_begin; tile_begin < blk_end; tile_begin += TILE) {
         const int valid = blk_end - tile_begin < TILE ? (int)(blk_end - tile_begin) : TILE;
-        const int wave_first = wave * WAVE_KEYS;
+        const bool full = valid == TILE;
 
-        K k[ITEMS];
-        uint32_t d[ITEMS];
-        uint32_t v[ITEMS];
-        if (valid == TILE) {
-#pragma unroll
-            for (int i = 0; i < ITEMS; ++i) {
-                const int local = wave_first + i * kWave + lane;
-                k[i] = keys_in[tile_begin + local];
-                if constexpr (PAIRS) v[i] = vals_in[tile_begin + local];
-            }
-#pragma unroll
-            for (int i = 0; i < ITEMS; ++i) {
-                if constexpr (ENCODE) k[i] = (K)encode_f32((uint32_t)k[i]);
-                d[i] = digit_of(k[i], shift, mask);
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < ITEMS; ++i) {
-                const int local = wave_first + i * kWave + lane;
-                if (local < valid) {
-                    K x = keys_in[tile_begin + local];
-                    if constexpr (ENCODE) x = (K)encode_f32((uint32_t)x);
-                    k[i] = x;
-                    d[i] = digit_of(x, shift, mask);
-                    if constexpr (PAIRS) v[i] = vals_in[tile_begin + local];
-                } else {
-                    k[i] = 0;
-                    d[i] = kRadix - 1;
-                    if constexpr (PAIRS) v[i] = 0u;
-                }
-            }
+        // Prefetch the next tile of the block; its loads are in flight while
+        // this tile is ranked and written.
+        K nxt[ITEMS];
+        const int64_t next_begin = tile_begin + TILE;
+        if (next_begin < blk_end) {
+            const int nvalid = blk_end - next_begin < TILE ? (int)(blk_end - next_begin) : TILE;
+            issue_tile_loads<K, ITEMS>(nxt, keys_in + next_begin, first, nvalid);
         }
+        uint32_t v[ITEMS];
+        if constexpr (PAIRS) issue_tile_loads<uint32_t, ITEMS>(v, vals_in + tile_begin, first, valid);
+        finish_tile<K, ENCODE, ITEMS>(cur, first, valid, full);
 
         // This wave's digit counters start at zero for the tile.
-#pragma unroll
-        for (int j = 0; j < kRadix / kWave; ++j) s.wave_count[wave][lane + j * kWave] = 0u;
+        reinterpret_cast<uint4 *>(s.wave_count[wave])[lane] = make_uint4(0u, 0u, 0u, 0u);
 
         // Rank within the wave: keys of earlier items (all lanes), then keys of
         // this item in lower lanes with the same digit.  The last lane of each
-        // same-digit group advances the wave's counter for that digit.
+        // same-digit group advances the wave's counter for that digit; the other
+        // lanes store into their own sink word, so there is no branch.
+        // The counter read is issued before the ballots so its latency hides
+        // under them; the scheduling fence keeps the compiler from hoisting
+        // every item's bit masks at once (which costs registers, not time).
         uint32_t r[ITEMS];
 #pragma unroll
         for (int i = 0; i < ITEMS; ++i) {
+            const uint32_t d = digit_of(cur[i], shift, mask);
+            uint32_t *counter = &s.wave_count[wave][d];
+            const uint32_t prior = *counter;
             uint32_t lo, hi;
-            match_digit(d[i], lo, hi);
+            match_digit(d, lo, hi);
             const uint32_t below = lanes_below(lo, hi);
             const uint32_t same = __popc(lo) + __popc(hi);
-            const uint32_t prior = s.wave_count[wave][d[i]];
-            if (below + 1u == same) s.wave_count[wave][d[i]] = prior + same;
-            r[i] = prior + below;
+            uint32_t *dst = (below + 1u == same) ? counter : &s.sink[wave][lane];
+            *dst = prior + same;
+            r[i] = (d << 16) | (prior + below);  // digit and rank (< 2^16) in one register
+            __builtin_amdgcn_sched_barrier(0);
         }
         __syncthreads();
 
-        // Per digit: exclusive prefix over waves, tile count, tile offset.
-        uint32_t tile_count = 0;
-        if (tid < kRadix) {
+        if (wave == 0) {
+            // Per digit (4 per lane): exclusive prefix over waves, the tile's
+            // count and its exclusive prefix over digits.
+            uint4 c[WAVES];
+            uint4 tot = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
             for (int w = 0; w < WAVES; ++w) {
-                const uint32_t c = s.wave_count[w][tid];
-                s.wave_count[w][tid] = tile_count;
-                tile_count += c;
+                c[w] = reinterpret_cast<const uint4 *>(s.wave_count[w])[lane];
+                const uint4 e = tot;
+                tot.x += c[w].x; tot.y += c[w].y; tot.z += c[w].z; tot.w += c[w].w;
+                c[w] = e;
             }
-        }
-        uint32_t tile_total;
-        const uint32_t tile_off = block_exclusive_scan<THREADS>(tile_count, s.scan_tmp, tile_total);
-        if (tid < kRadix) {
+            const uint4 off = wave_scan_digits(tot);
 #pragma unroll
-            for (int w = 0; w < WAVES; ++w) s.wave_count[w][tid] += tile_off;
-            const uint32_t run = s.run[tid];
-            s.out_base[tid] = run - tile_off;
-            const uint32_t pad = (tid == kRadix - 1) ? (uint32_t)(TILE - valid) : 0u;
-            s.run[tid] = run + tile_count - pad;
+            for (int w = 0; w < WAVES; ++w) {
+                reinterpret_cast<uint4 *>(s.wave_count[w])[lane] =
+                    make_uint4(c[w].x + off.x, c[w].y + off.y, c[w].z + off.z, c[w].w + off.w);
+            }
+            uint4 run = reinterpret_cast<const uint4 *>(s.run)[lane];
+            reinterpret_cast<uint4 *>(s.out_base)[lane] =
+                make_uint4(run.x - off.x, run.y - off.y, run.z - off.z, run.w - off.w);
+            // the padding slots of a short last tile were counted under digit `mask`
+            const uint32_t pad = (uint32_t)(TILE - valid);
+            const int d0 = 4 * lane;
+            run.x += tot.x - ((uint32_t)(d0 + 0) == mask ? pad : 0u);
+            run.y += tot.y - ((uint32_t)(d0 + 1) == mask ? pad : 0u);
+            run.z += tot.z - ((uint32_t)(d0 + 2) == mask ? pad : 0u);
+            run.w += tot.w - ((uint32_t)(d0 + 3) == mask ? pad : 0u);
+            reinterpret_cast<uint4 *>(s.run)[lane] = run;
         }
         __syncthreads();
 
         // Reorder the tile in LDS: slot = tile offset of the digit + rank.
-        uint32_t slot[ITEMS];
+#pragma unroll
+        for (int i = 0; i < ITEMS; ++i) r[i] = (r[i] & 0xFFFFu) + s.wave_count[wave][r[i] >> 16];
 #pragma unroll
         for (int i = 0; i < ITEMS; ++i) {
-            slot[i] = s.wave_count[wave][d[i]] + r[i];
-            s.x.keys[slot[i]] = k[i];
+            s.keys[r[i]] = cur[i];
+            if constexpr (PAIRS) s.vals[r[i]] = v[i];
         }
         __syncthreads();
 
         // Consecutive threads take consecutive slots: each digit's run of slots
-        // goes to consecutive global addresses.  The dest < n test never fails
-        // when the counts of upsweep and downsweep agree (same keys, same
-        // digit); it keeps a key array changed between the two kernels (a
-        // caller race) from turning into stores outside the output.
-        const uint32_t n32 = (uint32_t)n;
-        uint32_t dest[ITEMS];
+        // goes to consecutive global addresses.  With matching counts in
+        // upsweep and downsweep every dest is below n; the clamp (full tiles)
+        // and the test (short tile) only keep a key array changed between the
+        // two kernels by a racing caller from turning into stores outside the
+        // output.  Full tiles store unconditionally, so the compiler can count
+        // outstanding stores and need not drain them before the next tile.
+        if (full) {
 #pragma unroll
-        for (int i = 0; i < ITEMS; ++i) {
-            const int j = i * THREADS + tid;
-            dest[i] = n32;
-            if (j < valid) {
-                const K x = s.x.keys[j];
-                dest[i] = s.out_base[digit_of(x, shift, mask)] + (uint32_t)j;
+            for (int i = 0; i < ITEMS; ++i) {
+                const uint32_t j = (uint32_t)(i * THREADS + tid);
+                const K x = s.keys[j];
+                const uint32_t dest = min(s.out_base[digit_of(x, shift, mask)] + j, n32 - 1u);
                 K y = x;
                 if constexpr (DECODE) y = (K)decode_f32((uint32_t)x);
-                if (dest[i] < n32) keys_out[dest[i]] = y;
+                keys_out[dest] = y;
+                if constexpr (PAIRS) vals_out[dest] = s.vals[j];
             }
-        }
-        if constexpr (PAIRS) {
-            __syncthreads();
-#pragma unroll
-            for (int i = 0; i < ITEMS; ++i) s.x.vals[slot[i]] = v[i];
-            __syncthreads();
+        } else {
 #pragma unroll
             for (int i = 0; i < ITEMS; ++i) {
                 const int j = i * THREADS + tid;
-                if (j < valid && dest[i] < n32) vals_out[dest[i]] = s.x.vals[j];
+                if (j < valid) {
+                    const K x = s.keys[j];
+                    const uint32_t dest = s.out_base[digit_of(x, shift, mask)] + (uint32_t)j;
+                    K y = x;
+                    if constexpr (DECODE) y = (K)decode_f32((uint32_t)x);
+                    if (dest < n32) {
+                        keys_out[dest] = y;
+                        if constexpr (PAIRS) vals_out[dest] = s.vals[j];
+                    }
+                }
             }
         }
         __syncthreads();
+
+#pragma unroll
+        for (int i = 0; i < ITEMS; ++i) cur[i] = nxt[i];
     }
 }
 

@@ -34,7 +34,7 @@ using namespace lrs;
 enum KeyKind { KIND_U32 = 0, KIND_F32 = 1, KIND_U64 = 2 };
 
 constexpr int kMaxBlocks = 4096;  // count-matrix width cap (scan: 256 threads x 16)
-constexpr int kUpsweepThreads = 256;
+constexpr int kUpsweepThreads = 512;
 constexpr int kScanThreads = 256;
 constexpr int kScanPerThread = kMaxBlocks / kScanThreads;
 constexpr size_t kAlign = 256;
