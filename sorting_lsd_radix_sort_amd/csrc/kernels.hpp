@@ -273,14 +273,14 @@ __global__ __launch_bounds__(THREADS) void scan_kernel(uint32_t *__restrict__ co
 
 // ------------------------------------------------------------------ downsweep
 
-template <typename K, bool PAIRS, int WAVES, int ITEMS>
+template <typename K, bool PAIRS, int WAVES, int ITEMS, int SUB>
 struct DownsweepSmem {
     static constexpr int kThreads = WAVES * kWave;
     static constexpr int kTile = kThreads * ITEMS;
-    K keys[kTile];                                      // tile in digit order
-    uint32_t vals[PAIRS ? kTile : 1];                   // payload in digit order
+    K keys[SUB][kTile];                                 // SUB tiles, each in digit order
+    uint32_t vals[PAIRS ? SUB : 1][PAIRS ? kTile : 1];  // payload in the same order
     alignas(16) uint32_t wave_count[WAVES][kRadix];     // per-wave digit counts, then slot bases
-    alignas(16) uint32_t out_base[kRadix];              // global index of tile slot 0 of digit d
+    alignas(16) uint32_t out_base[SUB][kRadix];         // global index of tile slot 0 of digit d
     alignas(16) uint32_t run[kRadix];                   // next global index of digit d in this block
     uint32_t sink[WAVES][kWave];                        // stores of non-leader lanes land here
 };
@@ -329,14 +329,21 @@ __device__ __forceinline__ void finish_tile(K (&k)[ITEMS], int first, int valid,
 // w*64*ITEMS + i*64 + l, so each load instruction reads 64 consecutive keys and
 // (item, lane) order is input order.  The next tile's keys are loaded into
 // registers while the current tile is ranked and written.
-template <typename K, bool PAIRS, int WAVES, int ITEMS, bool ENCODE, bool DECODE>
+//
+// SUB consecutive tiles are ranked and reordered into SUB LDS regions before
+// they are written out together.  A digit's runs from consecutive tiles are
+// adjacent in the output, so the output line they share is completed by two
+// stores issued back to back (merged in L2) instead of one tile apart: the
+// store stream behaves like runs SUB times longer, with the registers of one
+// tile.
+template <typename K, bool PAIRS, int WAVES, int ITEMS, int SUB, bool ENCODE, bool DECODE>
 __global__ __launch_bounds__(WAVES * kWave) void downsweep_kernel(
     const K *__restrict__ keys_in, K *__restrict__ keys_out, const uint32_t *__restrict__ vals_in,
     uint32_t *__restrict__ vals_out, const uint32_t *__restrict__ counts,
     const uint32_t *__restrict__ row_total, int64_t n, int64_t block_len, int num_blocks, int shift,
     uint32_t mask)
 {
-    using Smem = DownsweepSmem<K, PAIRS, WAVES, ITEMS>;
+    using Smem = DownsweepSmem<K, PAIRS, WAVES, ITEMS, SUB>;
     constexpr int THREADS = Smem::kThreads;
     constexpr int TILE = Smem::kTile;
     constexpr int WAVE_KEYS = kWave * ITEMS;
@@ -373,15 +380,23 @@ __global__ __launch_bounds__(WAVES * kWave) void downsweep_kernel(
         issue_tile_loads<K, ITEMS>(cur, keys_in + blk_begin, first, valid0);
     }
 
+    int sub = 0;  // region of this tile within the current group of SUB tiles
     for (int64_t tile_begin = blk_begin; tile_begin < blk_end; tile_begin += TILE) {
         const int valid = blk_end - tile_begin < TILE ? (int)(blk_end - tile_begin) : TILE;
         const bool full = valid == TILE;
+        const bool last = tile_begin + TILE >= blk_end;
+        // Lane indices re-derived from an opaque copy each tile: the per-item
+        // offsets built from them then fold into the instructions that use
+        // them instead of being hoisted out of the loop into ~50 registers.
+        int tid_l = tid;
+        asm volatile("" : "+v"(tid_l));
+        const int first = (tid_l / kWave) * WAVE_KEYS + (tid_l & (kWave - 1));
 
         // Prefetch the next tile of the block; its loads are in flight while
         // this tile is ranked and written.
         K nxt[ITEMS];
         const int64_t next_begin = tile_begin + TILE;
-        if (next_begin < blk_end) {
+        if (!last) {
             const int nvalid = blk_end - next_begin < TILE ? (int)(blk_end - next_begin) : TILE;
             issue_tile_loads<K, ITEMS>(nxt, keys_in + next_begin, first, nvalid);
         }
@@ -389,7 +404,8 @@ __global__ __launch_bounds__(WAVES * kWave) void downsweep_kernel(
         if constexpr (PAIRS) issue_tile_loads<uint32_t, ITEMS>(v, vals_in + tile_begin, first, valid);
         finish_tile<K, ENCODE, ITEMS>(cur, first, valid, full);
 
-        // This wave's digit counters start at zero for the tile.
+        // This wave's digit counters start at zero for the tile.  (The
+        // previous tile's readers of these counters are this wave itself.)
         reinterpret_cast<uint4 *>(s.wave_count[wave])[lane] = make_uint4(0u, 0u, 0u, 0u);
 
         // Rank within the wave: keys of earlier items (all lanes), then keys of
@@ -435,7 +451,7 @@ __global__ __launch_bounds__(WAVES * kWave) void downsweep_kernel(
                     make_uint4(c[w].x + off.x, c[w].y + off.y, c[w].z + off.z, c[w].w + off.w);
             }
             uint4 run = reinterpret_cast<const uint4 *>(s.run)[lane];
-            reinterpret_cast<uint4 *>(s.out_base)[lane] =
+            reinterpret_cast<uint4 *>(s.out_base[sub])[lane] =
                 make_uint4(run.x - off.x, run.y - off.y, run.z - off.z, run.w - off.w);
             // the padding slots of a short last tile were counted under digit `mask`
             const uint32_t pad = (uint32_t)(TILE - valid);
@@ -453,41 +469,297 @@ __global__ __launch_bounds__(WAVES * kWave) void downsweep_kernel(
         for (int i = 0; i < ITEMS; ++i) r[i] = (r[i] & 0xFFFFu) + s.wave_count[wave][r[i] >> 16];
 #pragma unroll
         for (int i = 0; i < ITEMS; ++i) {
-            s.keys[r[i]] = cur[i];
-            if constexpr (PAIRS) s.vals[r[i]] = v[i];
+            s.keys[sub][r[i]] = cur[i];
+            if constexpr (PAIRS) s.vals[sub][r[i]] = v[i];
+        }
+
+        if (sub == SUB - 1 || last) {
+            // The next tile's keys are used here, before any store is issued:
+            // waiting for them after the stores would wait for the stores too.
+            if (!last) {
+#pragma unroll
+                for (int i = 0; i < ITEMS; ++i) asm volatile("" : "+v"(nxt[i]));
+            }
+            __syncthreads();
+
+            // Consecutive threads take consecutive slots: each digit's run of
+            // slots goes to consecutive global addresses.  With matching counts
+            // in upsweep and downsweep every dest is below n; the clamp (full
+            // tiles) and the test (short tile) only keep a key array changed
+            // between the two kernels by a racing caller from turning into
+            // stores outside the output.  Only the block's last tile can be
+            // short.  No barrier follows: the LDS read here is next written
+            // after the next tile's rank barrier.
+            for (int t = 0; t <= sub; ++t) {
+                if (!last || t < sub || full) {
+#pragma unroll
+                    for (int i = 0; i < ITEMS; ++i) {
+                        const uint32_t j = (uint32_t)(i * THREADS + tid_l);
+                        const K x = s.keys[t][j];
+                        const uint32_t dest = min(s.out_base[t][digit_of(x, shift, mask)] + j, n32 - 1u);
+                        K y = x;
+                        if constexpr (DECODE) y = (K)decode_f32((uint32_t)x);
+                        keys_out[dest] = y;
+                        if constexpr (PAIRS) vals_out[dest] = s.vals[t][j];
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < ITEMS; ++i) {
+                        const int j = i * THREADS + tid_l;
+                        if (j < valid) {
+                            const K x = s.keys[t][j];
+                            const uint32_t dest = s.out_base[t][digit_of(x, shift, mask)] + (uint32_t)j;
+                            K y = x;
+                            if constexpr (DECODE) y = (K)decode_f32((uint32_t)x);
+                            if (dest < n32) {
+                                keys_out[dest] = y;
+                                if constexpr (PAIRS) vals_out[dest] = s.vals[t][j];
+                            }
+                        }
+                    }
+                }
+            }
+            sub = 0;
+        } else {
+            ++sub;
+        }
+
+#pragma unroll
+        for (int i = 0; i < ITEMS; ++i) cur[i] = nxt[i];
+    }
+}
+
+// --------------------------------------------------- write-combining downsweep
+
+// Output lines: LE consecutive output positions starting at a multiple of LE
+// (128 bytes of keys for LE = 128 / sizeof(K)).  Stores of whole aligned lines
+// run at close to streaming speed on this memory system, while the ~16-key
+// runs a 4096-key tile gives each digit land at arbitrary offsets and cost
+// partial-line writes.  So each workgroup keeps, per digit, the keys of the
+// output line it has started but not finished (the "carry") in LDS across
+// tiles, and stores only complete lines; the block's last tile stores the
+// remainder.  Lines shared with the neighbouring blocks (the first and last
+// line of each digit's range) are written partially, each byte once.
+template <typename K, bool PAIRS, int WAVES, int ITEMS, int LE>
+struct WcSmem {
+    static constexpr int kThreads = WAVES * kWave;
+    static constexpr int kTile = kThreads * ITEMS;
+    // most lines one tile can emit: pending + new keys of all digits, plus a
+    // partial line at each end of every digit's range
+    static constexpr int kMaxItems = (kTile + kRadix * (LE - 1)) / LE + 2 * kRadix;
+    K keys[kTile];                           // tile in digit order
+    uint32_t vals[PAIRS ? kTile : 1];
+    K ckeys[kRadix][LE];                     // carry: slot e holds output position = e (mod LE)
+    uint32_t cvals[PAIRS ? kRadix : 1][LE];
+    alignas(16) uint32_t wave_count[WAVES][kRadix];
+    alignas(16) uint32_t run[kRadix];        // next output position of digit d in this block
+    alignas(16) uint32_t bstart[kRadix];     // first output position of digit d in this block
+    alignas(16) uint4 info[kRadix];          // {line base, first new position, slot - position, end}
+    alignas(8) uint2 tail[kRadix];           // {first tile slot still pending, position - slot}
+    uint32_t sink[WAVES][kWave];
+    uint32_t n_items;
+    uint8_t owner[kMaxItems];                // digit of each line to store this tile
+};
+
+template <typename K, bool PAIRS, int WAVES, int ITEMS, int LE, bool ENCODE, bool DECODE>
+__global__ __launch_bounds__(WAVES * kWave) void downsweep_wc_kernel(
+    const K *__restrict__ keys_in, K *__restrict__ keys_out, const uint32_t *__restrict__ vals_in,
+    uint32_t *__restrict__ vals_out, const uint32_t *__restrict__ counts,
+    const uint32_t *__restrict__ row_total, int64_t n, int64_t block_len, int num_blocks, int shift,
+    uint32_t mask)
+{
+    using Smem = WcSmem<K, PAIRS, WAVES, ITEMS, LE>;
+    constexpr int THREADS = Smem::kThreads;
+    constexpr int TILE = Smem::kTile;
+    constexpr int WAVE_KEYS = kWave * ITEMS;
+    constexpr int IPW = kWave / LE;  // lines per wave instruction
+    static_assert(THREADS >= kRadix, "one thread per digit is assumed");
+    static_assert(TILE <= 65536, "ranks are packed in 16 bits");
+    static_assert(LE == 8 || LE == 16 || LE == 32 || LE == 64, "a line is a power-of-two part of a wave");
+    static_assert(Smem::kMaxItems < 65536, "line indices");
+    __shared__ Smem s;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int blk = blockIdx.x;
+    const int64_t blk_begin = (int64_t)blk * block_len;
+    const int64_t blk_end = blk_begin + block_len < n ? blk_begin + block_len : n;
+    const uint32_t n32 = (uint32_t)n;
+
+    if (wave == 0) {
+        const uint4 tot = reinterpret_cast<const uint4 *>(row_total)[lane];
+        const uint4 start = wave_scan_digits(tot);
+        const int d0 = 4 * lane;
+        uint4 r;
+        r.x = start.x + counts[(int64_t)(d0 + 0) * num_blocks + blk];
+        r.y = start.y + counts[(int64_t)(d0 + 1) * num_blocks + blk];
+        r.z = start.z + counts[(int64_t)(d0 + 2) * num_blocks + blk];
+        r.w = start.w + counts[(int64_t)(d0 + 3) * num_blocks + blk];
+        reinterpret_cast<uint4 *>(s.run)[lane] = r;
+        reinterpret_cast<uint4 *>(s.bstart)[lane] = r;
+    }
+
+    K cur[ITEMS];
+    {
+        const int valid0 = blk_end - blk_begin < TILE ? (int)(blk_end - blk_begin) : TILE;
+        issue_tile_loads<K, ITEMS>(cur, keys_in + blk_begin, wave * WAVE_KEYS + lane, valid0);
+    }
+
+    for (int64_t tile_begin = blk_begin; tile_begin < blk_end; tile_begin += TILE) {
+        const int valid = blk_end - tile_begin < TILE ? (int)(blk_end - tile_begin) : TILE;
+        const bool full = valid == TILE;
+        const bool last = tile_begin + TILE >= blk_end;
+        int tid_l = tid;
+        asm volatile("" : "+v"(tid_l));
+        const int first = (tid_l / kWave) * WAVE_KEYS + (tid_l & (kWave - 1));
+
+        K nxt[ITEMS];
+        const int64_t next_begin = tile_begin + TILE;
+        if (!last) {
+            const int nvalid = blk_end - next_begin < TILE ? (int)(blk_end - next_begin) : TILE;
+            issue_tile_loads<K, ITEMS>(nxt, keys_in + next_begin, first, nvalid);
+        }
+        uint32_t v[ITEMS];
+        if constexpr (PAIRS) issue_tile_loads<uint32_t, ITEMS>(v, vals_in + tile_begin, first, valid);
+        finish_tile<K, ENCODE, ITEMS>(cur, first, valid, full);
+
+        // Carry the previous tile's unfinished lines: its keys are still in
+        // LDS (this tile's keys overwrite them only after two barriers).  The
+        // previous tile was full and not the block's last.
+        if (tile_begin != blk_begin) {
+#pragma unroll
+            for (int i = 0; i < ITEMS; ++i) {
+                const uint32_t j = (uint32_t)(i * THREADS + tid_l);
+                const K x = s.keys[j];
+                const uint32_t d = digit_of(x, shift, mask);
+                const uint2 t = s.tail[d];
+                if (j >= t.x) {
+                    const uint32_t e = (j + t.y) & (uint32_t)(LE - 1);
+                    s.ckeys[d][e] = x;
+                    if constexpr (PAIRS) s.cvals[d][e] = s.vals[j];
+                }
+            }
+        }
+
+#pragma unroll
+        for (int j = 0; j < kRadix / kWave; ++j) s.wave_count[wave][lane + j * kWave] = 0u;
+
+        uint32_t r[ITEMS];
+#pragma unroll
+        for (int i = 0; i < ITEMS; ++i) {
+            const uint32_t d = digit_of(cur[i], shift, mask);
+            uint32_t *counter = &s.wave_count[wave][d];
+            const uint32_t prior = *counter;
+            uint32_t lo, hi;
+            match_digit(d, lo, hi);
+            const uint32_t below = lanes_below(lo, hi);
+            const uint32_t same = __popc(lo) + __popc(hi);
+            uint32_t *dst = (below + 1u == same) ? counter : &s.sink[wave][lane];
+            *dst = prior + same;
+            r[i] = (d << 16) | (prior + below);
+            __builtin_amdgcn_sched_barrier(0);
         }
         __syncthreads();
 
-        // Consecutive threads take consecutive slots: each digit's run of slots
-        // goes to consecutive global addresses.  With matching counts in
-        // upsweep and downsweep every dest is below n; the clamp (full tiles)
-        // and the test (short tile) only keep a key array changed between the
-        // two kernels by a racing caller from turning into stores outside the
-        // output.  Full tiles store unconditionally, so the compiler can count
-        // outstanding stores and need not drain them before the next tile.
-        if (full) {
+        if (wave == 0) {
+            uint4 c[WAVES];
+            uint4 tot = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-            for (int i = 0; i < ITEMS; ++i) {
-                const uint32_t j = (uint32_t)(i * THREADS + tid);
-                const K x = s.keys[j];
-                const uint32_t dest = min(s.out_base[digit_of(x, shift, mask)] + j, n32 - 1u);
-                K y = x;
-                if constexpr (DECODE) y = (K)decode_f32((uint32_t)x);
-                keys_out[dest] = y;
-                if constexpr (PAIRS) vals_out[dest] = s.vals[j];
+            for (int w = 0; w < WAVES; ++w) {
+                c[w] = reinterpret_cast<const uint4 *>(s.wave_count[w])[lane];
+                const uint4 e = tot;
+                tot.x += c[w].x; tot.y += c[w].y; tot.z += c[w].z; tot.w += c[w].w;
+                c[w] = e;
             }
-        } else {
+            const uint4 off = wave_scan_digits(tot);
 #pragma unroll
-            for (int i = 0; i < ITEMS; ++i) {
-                const int j = i * THREADS + tid;
-                if (j < valid) {
-                    const K x = s.keys[j];
-                    const uint32_t dest = s.out_base[digit_of(x, shift, mask)] + (uint32_t)j;
-                    K y = x;
-                    if constexpr (DECODE) y = (K)decode_f32((uint32_t)x);
-                    if (dest < n32) {
-                        keys_out[dest] = y;
-                        if constexpr (PAIRS) vals_out[dest] = s.vals[j];
+            for (int w = 0; w < WAVES; ++w) {
+                reinterpret_cast<uint4 *>(s.wave_count[w])[lane] =
+                    make_uint4(c[w].x + off.x, c[w].y + off.y, c[w].z + off.z, c[w].w + off.w);
+            }
+            const uint4 run = reinterpret_cast<const uint4 *>(s.run)[lane];
+            const uint4 bst = reinterpret_cast<const uint4 *>(s.bstart)[lane];
+            const uint32_t pad = (uint32_t)(TILE - valid);
+            const int d0 = 4 * lane;
+            const uint32_t cnt[4] = {tot.x, tot.y, tot.z, tot.w};
+            const uint32_t toff[4] = {off.x, off.y, off.z, off.w};
+            const uint32_t rb[4] = {run.x, run.y, run.z, run.w};
+            const uint32_t bs[4] = {bst.x, bst.y, bst.z, bst.w};
+            uint32_t items[4], hi[4], line0[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                // padding slots of a short last tile were counted under digit `mask`
+                const uint32_t real = cnt[k] - ((uint32_t)(d0 + k) == mask ? pad : 0u);
+                hi[k] = rb[k] + real;
+                const uint32_t lo = max(rb[k] & ~(uint32_t)(LE - 1), bs[k]);
+                line0[k] = lo & ~(uint32_t)(LE - 1);
+                if (last)
+                    items[k] = hi[k] > lo ? (hi[k] + LE - 1) / LE - lo / LE : 0u;
+                else
+                    items[k] = hi[k] / LE - lo / LE;
+            }
+            const uint4 ioff = wave_scan_digits(make_uint4(items[0], items[1], items[2], items[3]));
+            const uint32_t io[4] = {ioff.x, ioff.y, ioff.z, ioff.w};
+            uint4 inf[4];
+            uint2 tl[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                inf[k] = make_uint4(line0[k] - io[k] * (uint32_t)LE, rb[k], toff[k] - rb[k], hi[k]);
+                const uint32_t pend_from = max(hi[k] & ~(uint32_t)(LE - 1), rb[k]);
+                tl[k] = make_uint2(toff[k] + (pend_from - rb[k]), rb[k] - toff[k]);
+                for (uint32_t q = 0; q < items[k]; ++q) s.owner[io[k] + q] = (uint8_t)(d0 + k);
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                s.info[d0 + k] = inf[k];
+                s.tail[d0 + k] = tl[k];
+            }
+            reinterpret_cast<uint4 *>(s.run)[lane] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+            if (lane == kWave - 1) s.n_items = io[3] + items[3];
+        }
+        __syncthreads();
+
+#pragma unroll
+        for (int i = 0; i < ITEMS; ++i) r[i] = (r[i] & 0xFFFFu) + s.wave_count[wave][r[i] >> 16];
+#pragma unroll
+        for (int i = 0; i < ITEMS; ++i) {
+            s.keys[r[i]] = cur[i];
+            if constexpr (PAIRS) s.vals[r[i]] = v[i];
+        }
+        // The next tile's keys are used here, before any store of this tile
+        // is issued: waiting for them later would also wait for every store.
+        if (!last) {
+#pragma unroll
+            for (int i = 0; i < ITEMS; ++i) asm volatile("" : "+v"(nxt[i]));
+        }
+        __syncthreads();
+
+        // Store the complete lines: lane e of line group g writes output
+        // position base + q*LE + e of line q, taking the key from the carry
+        // (positions before this tile's first key of the digit) or the tile.
+        {
+            const uint32_t total = s.n_items;
+            const uint32_t g = (uint32_t)(tid_l & (kWave - 1)) / LE;
+            const uint32_t e = (uint32_t)(tid_l & (LE - 1));
+            for (uint32_t q0 = (uint32_t)(tid_l / kWave) * IPW; q0 < total; q0 += WAVES * IPW) {
+                const uint32_t q = q0 + g;
+                if (q < total) {
+                    const uint32_t d = s.owner[q];
+                    const uint4 f = s.info[d];
+                    const uint32_t p = f.x + q * (uint32_t)LE + e;
+                    if (p >= s.bstart[d] && p < f.w) {
+                        const bool from_carry = p < f.y;
+                        const uint32_t slot = p + f.z;
+                        const K *ksrc = from_carry ? &s.ckeys[d][e] : &s.keys[slot];
+                        K x = *ksrc;
+                        if constexpr (DECODE) x = (K)decode_f32((uint32_t)x);
+                        const uint32_t dest = min(p, n32 - 1u);
+                        keys_out[dest] = x;
+                        if constexpr (PAIRS) {
+                            const uint32_t *vsrc = from_carry ? &s.cvals[d][e] : &s.vals[slot];
+                            vals_out[dest] = *vsrc;
+                        }
                     }
                 }
             }

@@ -264,13 +264,56 @@ hipError_t launch_scan(uint32_t *counts, uint32_t *rowtot, int blocks, hipStream
     });
 }
 
+// Output line length (elements) of the write-combining downsweep per key type:
+// 128-byte key lines; 0 selects the plain downsweep.
+template <typename K, bool PAIRS>
+constexpr int line_elems()
+{
+#ifdef LRS_LINE_U32
+    if constexpr (sizeof(K) == 4 && !PAIRS) return LRS_LINE_U32;
+#endif
+#ifdef LRS_LINE_U32P
+    if constexpr (sizeof(K) == 4 && PAIRS) return LRS_LINE_U32P;
+#endif
+#ifdef LRS_LINE_U64
+    if constexpr (sizeof(K) == 8) return LRS_LINE_U64;
+#endif
+    return 0;
+}
+
+// Tiles written out together by the plain downsweep: as many as fit in a
+// 64 KB budget of tile LDS (more would cut occupancy below two workgroups).
+template <typename K, bool PAIRS>
+constexpr int sub_tiles()
+{
+#ifdef LRS_SUB
+    constexpr int want = LRS_SUB;
+#else
+    constexpr int want = 2;
+#endif
+    constexpr int tile_bytes = (sizeof(K) == 8 ? kWaves64 * 64 * kItems64 : kWaves32 * 64 * kItems32) *
+                               (int)(sizeof(K) + (PAIRS ? 4 : 0));
+    constexpr int fit = (64 * 1024) / tile_bytes;
+    return want < fit ? want : (fit > 0 ? fit : 1);
+}
+
+template <typename K, bool PAIRS, int WAVES, int ITEMS, bool ENCODE, bool DECODE>
+auto downsweep_fn()
+{
+    constexpr int LE = line_elems<K, PAIRS>();
+    if constexpr (LE > 0)
+        return downsweep_wc_kernel<K, PAIRS, WAVES, ITEMS, LE, ENCODE, DECODE>;
+    else
+        return downsweep_kernel<K, PAIRS, WAVES, ITEMS, sub_tiles<K, PAIRS>(), ENCODE, DECODE>;
+}
+
 template <typename K, bool PAIRS, int WAVES, int ITEMS, bool ENCODE, bool DECODE>
 hipError_t launch_downsweep(const K *kin, K *kout, const uint32_t *vin, uint32_t *vout, const uint32_t *counts,
                             const uint32_t *rowtot, int64_t n, int64_t block_len, int blocks, int shift,
                             uint32_t mask, hipStream_t stream)
 {
     return launch(LRS_KERNEL_DOWNSWEEP, stream, [&] {
-        downsweep_kernel<K, PAIRS, WAVES, ITEMS, ENCODE, DECODE><<<blocks, WAVES * 64, 0, stream>>>(
+        downsweep_fn<K, PAIRS, WAVES, ITEMS, ENCODE, DECODE>()<<<blocks, WAVES * 64, 0, stream>>>(
             kin, kout, vin, vout, counts, rowtot, n, block_len, blocks, shift, mask);
     });
 }
@@ -302,7 +345,7 @@ hipError_t blocks_for(int64_t tiles, int *blocks)
     int cus = 0, per_cu = 0;
     hipError_t err = device_cus(&cus);
     if (err != hipSuccess) return err;
-    err = occupancy(downsweep_kernel<K, PAIRS, WAVES, ITEMS, false, false>, WAVES * 64, &per_cu);
+    err = occupancy(downsweep_fn<K, PAIRS, WAVES, ITEMS, false, false>(), WAVES * 64, &per_cu);
     if (err != hipSuccess) return err;
     const int64_t want = std::max<int64_t>(1, (int64_t)cus * per_cu);
     *blocks = (int)std::min<int64_t>(std::min<int64_t>(tiles, want), kMaxBlocks);
