@@ -19,8 +19,8 @@
 //
 // Counting per block of many tiles instead of per tile keeps the count matrix a
 // few MB at any n (so the scan is cheap), and lets a workgroup continue each
-// digit's output run from one tile to the next, so partial cache lines at a
-// run's end are completed by the same workgroup through its own L2.
+// digit's output run from one tile to the next, so a partial cache line at a
+// run's end is completed by the same workgroup soon after.
 //
 // Stability: within a tile, key i's rank among equal digits counts only keys
 // before it in input order (the page's section 3, last paragraphs: the stable
@@ -122,11 +122,6 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x)
     return x;
 }
 
-__device__ __forceinline__ uint32_t wave_broadcast_last(uint32_t x)
-{
-    return __builtin_amdgcn_readlane(x, kWave - 1);
-}
-
 // Exclusive prefix sum of one value per thread over the whole workgroup.
 // s_tmp needs THREADS/64 words.  Every thread must call it (it synchronizes).
 template <int THREADS>
@@ -152,7 +147,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *s
 
 // Exclusive prefix sum over the 256 digits, run by one wave: lane l owns
 // digits 4l..4l+3 (one 16-byte vector).  Returns the lane's four exclusive
-// prefixes; `lane_total` is the sum of its four inputs.
+// prefixes.
 __device__ __forceinline__ uint4 wave_scan_digits(uint4 c)
 {
     const uint32_t p1 = c.x, p2 = p1 + c.y, p3 = p2 + c.z, sum = p3 + c.w;
@@ -279,10 +274,13 @@ struct DownsweepSmem {
     static constexpr int kTile = kThreads * ITEMS;
     K keys[SUB][kTile];                                 // SUB tiles, each in digit order
     uint32_t vals[PAIRS ? SUB : 1][PAIRS ? kTile : 1];  // payload in the same order
-    alignas(16) uint32_t wave_count[WAVES][kRadix];     // per-wave digit counts, then slot bases
+    // Per-wave 16-bit digit counters, two buffers alternating by tile: the
+    // current tile counts in one; in the other, each wave's own row holds its
+    // slot bases (tile slot of its first key of digit d) for the scatter.
+    alignas(16) uint16_t wave_count[2][WAVES][kRadix];
     alignas(16) uint32_t out_base[SUB][kRadix];         // global index of tile slot 0 of digit d
     alignas(16) uint32_t run[kRadix];                   // next global index of digit d in this block
-    uint32_t sink[WAVES][kWave];                        // stores of non-leader lanes land here
+    uint16_t sink[WAVES][kWave];                        // stores of non-leader lanes land here
 };
 
 // Issues the loads of one tile's keys for this lane: item i is key
@@ -348,7 +346,7 @@ __global__ __launch_bounds__(WAVES * kWave) void downsweep_kernel(
     constexpr int TILE = Smem::kTile;
     constexpr int WAVE_KEYS = kWave * ITEMS;
     static_assert(THREADS >= kRadix, "one thread per digit is assumed");
-    static_assert(TILE <= 65536, "ranks are packed in 16 bits");
+    static_assert(TILE < 65536, "ranks and counters are 16-bit");
     __shared__ Smem s;
 
     const int tid = threadIdx.x;
@@ -404,9 +402,16 @@ __global__ __launch_bounds__(WAVES * kWave) void downsweep_kernel(
         if constexpr (PAIRS) issue_tile_loads<uint32_t, ITEMS>(v, vals_in + tile_begin, first, valid);
         finish_tile<K, ENCODE, ITEMS>(cur, first, valid, full);
 
-        // This wave's digit counters start at zero for the tile.  (The
-        // previous tile's readers of these counters are this wave itself.)
-        reinterpret_cast<uint4 *>(s.wave_count[wave])[lane] = make_uint4(0u, 0u, 0u, 0u);
+        // This wave's digit counters start at zero for the tile.  Counters
+        // alternate between two buffers by tile parity: the other waves read
+        // this tile's counters after the barrier below, and the row being
+        // cleared was last read by other waves in the tile before the
+        // previous one (finished before the previous barrier) and by this
+        // wave itself, as slot bases, in the previous tile.
+        const int par = (int)(((tile_begin - blk_begin) / TILE) & 1);
+        uint16_t(&count)[WAVES][kRadix] = s.wave_count[par];
+        uint16_t(&slot_base)[WAVES][kRadix] = s.wave_count[par ^ 1];
+        reinterpret_cast<uint2 *>(count[wave])[lane] = make_uint2(0u, 0u);
 
         // Rank within the wave: keys of earlier items (all lanes), then keys of
         // this item in lower lanes with the same digit.  The last lane of each
@@ -419,54 +424,54 @@ __global__ __launch_bounds__(WAVES * kWave) void downsweep_kernel(
 #pragma unroll
         for (int i = 0; i < ITEMS; ++i) {
             const uint32_t d = digit_of(cur[i], shift, mask);
-            uint32_t *counter = &s.wave_count[wave][d];
+            uint16_t *counter = &count[wave][d];
             const uint32_t prior = *counter;
             uint32_t lo, hi;
             match_digit(d, lo, hi);
             const uint32_t below = lanes_below(lo, hi);
             const uint32_t same = __popc(lo) + __popc(hi);
-            uint32_t *dst = (below + 1u == same) ? counter : &s.sink[wave][lane];
-            *dst = prior + same;
+            uint16_t *dst = (below + 1u == same) ? counter : &s.sink[wave][lane];
+            *dst = (uint16_t)(prior + same);
             r[i] = (d << 16) | (prior + below);  // digit and rank (< 2^16) in one register
             __builtin_amdgcn_sched_barrier(0);
         }
         __syncthreads();
 
-        if (wave == 0) {
-            // Per digit (4 per lane): exclusive prefix over waves, the tile's
-            // count and its exclusive prefix over digits.
-            uint4 c[WAVES];
+        {
+            // Every wave forms the digit offsets itself (4 digits per lane):
+            // its own prefix over the waves before it, and the tile's
+            // exclusive prefix over digits.  Redundant across waves, but it
+            // needs no second barrier and no wave waits for another.
+            uint4 before = make_uint4(0u, 0u, 0u, 0u);
             uint4 tot = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
             for (int w = 0; w < WAVES; ++w) {
-                c[w] = reinterpret_cast<const uint4 *>(s.wave_count[w])[lane];
-                const uint4 e = tot;
-                tot.x += c[w].x; tot.y += c[w].y; tot.z += c[w].z; tot.w += c[w].w;
-                c[w] = e;
+                const uint2 c = reinterpret_cast<const uint2 *>(count[w])[lane];
+                if (w == wave) before = tot;
+                tot.x += c.x & 0xFFFFu; tot.y += c.x >> 16; tot.z += c.y & 0xFFFFu; tot.w += c.y >> 16;
             }
             const uint4 off = wave_scan_digits(tot);
-#pragma unroll
-            for (int w = 0; w < WAVES; ++w) {
-                reinterpret_cast<uint4 *>(s.wave_count[w])[lane] =
-                    make_uint4(c[w].x + off.x, c[w].y + off.y, c[w].z + off.z, c[w].w + off.w);
+            reinterpret_cast<uint2 *>(slot_base[wave])[lane] =
+                make_uint2((before.x + off.x) | ((before.y + off.y) << 16),
+                           (before.z + off.z) | ((before.w + off.w) << 16));
+            if (wave == 0) {
+                uint4 run = reinterpret_cast<const uint4 *>(s.run)[lane];
+                reinterpret_cast<uint4 *>(s.out_base[sub])[lane] =
+                    make_uint4(run.x - off.x, run.y - off.y, run.z - off.z, run.w - off.w);
+                // the padding slots of a short last tile were counted under digit `mask`
+                const uint32_t pad = (uint32_t)(TILE - valid);
+                const int d0 = 4 * lane;
+                run.x += tot.x - ((uint32_t)(d0 + 0) == mask ? pad : 0u);
+                run.y += tot.y - ((uint32_t)(d0 + 1) == mask ? pad : 0u);
+                run.z += tot.z - ((uint32_t)(d0 + 2) == mask ? pad : 0u);
+                run.w += tot.w - ((uint32_t)(d0 + 3) == mask ? pad : 0u);
+                reinterpret_cast<uint4 *>(s.run)[lane] = run;
             }
-            uint4 run = reinterpret_cast<const uint4 *>(s.run)[lane];
-            reinterpret_cast<uint4 *>(s.out_base[sub])[lane] =
-                make_uint4(run.x - off.x, run.y - off.y, run.z - off.z, run.w - off.w);
-            // the padding slots of a short last tile were counted under digit `mask`
-            const uint32_t pad = (uint32_t)(TILE - valid);
-            const int d0 = 4 * lane;
-            run.x += tot.x - ((uint32_t)(d0 + 0) == mask ? pad : 0u);
-            run.y += tot.y - ((uint32_t)(d0 + 1) == mask ? pad : 0u);
-            run.z += tot.z - ((uint32_t)(d0 + 2) == mask ? pad : 0u);
-            run.w += tot.w - ((uint32_t)(d0 + 3) == mask ? pad : 0u);
-            reinterpret_cast<uint4 *>(s.run)[lane] = run;
         }
-        __syncthreads();
 
         // Reorder the tile in LDS: slot = tile offset of the digit + rank.
 #pragma unroll
-        for (int i = 0; i < ITEMS; ++i) r[i] = (r[i] & 0xFFFFu) + s.wave_count[wave][r[i] >> 16];
+        for (int i = 0; i < ITEMS; ++i) r[i] = (r[i] & 0xFFFFu) + slot_base[wave][r[i] >> 16];
 #pragma unroll
         for (int i = 0; i < ITEMS; ++i) {
             s.keys[sub][r[i]] = cur[i];
@@ -523,248 +528,6 @@ __global__ __launch_bounds__(WAVES * kWave) void downsweep_kernel(
         } else {
             ++sub;
         }
-
-#pragma unroll
-        for (int i = 0; i < ITEMS; ++i) cur[i] = nxt[i];
-    }
-}
-
-// --------------------------------------------------- write-combining downsweep
-
-// Output lines: LE consecutive output positions starting at a multiple of LE
-// (128 bytes of keys for LE = 128 / sizeof(K)).  Stores of whole aligned lines
-// run at close to streaming speed on this memory system, while the ~16-key
-// runs a 4096-key tile gives each digit land at arbitrary offsets and cost
-// partial-line writes.  So each workgroup keeps, per digit, the keys of the
-// output line it has started but not finished (the "carry") in LDS across
-// tiles, and stores only complete lines; the block's last tile stores the
-// remainder.  Lines shared with the neighbouring blocks (the first and last
-// line of each digit's range) are written partially, each byte once.
-template <typename K, bool PAIRS, int WAVES, int ITEMS, int LE>
-struct WcSmem {
-    static constexpr int kThreads = WAVES * kWave;
-    static constexpr int kTile = kThreads * ITEMS;
-    // most lines one tile can emit: pending + new keys of all digits, plus a
-    // partial line at each end of every digit's range
-    static constexpr int kMaxItems = (kTile + kRadix * (LE - 1)) / LE + 2 * kRadix;
-    K keys[kTile];                           // tile in digit order
-    uint32_t vals[PAIRS ? kTile : 1];
-    K ckeys[kRadix][LE];                     // carry: slot e holds output position = e (mod LE)
-    uint32_t cvals[PAIRS ? kRadix : 1][LE];
-    alignas(16) uint32_t wave_count[WAVES][kRadix];
-    alignas(16) uint32_t run[kRadix];        // next output position of digit d in this block
-    alignas(16) uint32_t bstart[kRadix];     // first output position of digit d in this block
-    alignas(16) uint4 info[kRadix];          // {line base, first new position, slot - position, end}
-    alignas(8) uint2 tail[kRadix];           // {first tile slot still pending, position - slot}
-    uint32_t sink[WAVES][kWave];
-    uint32_t n_items;
-    uint8_t owner[kMaxItems];                // digit of each line to store this tile
-};
-
-template <typename K, bool PAIRS, int WAVES, int ITEMS, int LE, bool ENCODE, bool DECODE>
-__global__ __launch_bounds__(WAVES * kWave) void downsweep_wc_kernel(
-    const K *__restrict__ keys_in, K *__restrict__ keys_out, const uint32_t *__restrict__ vals_in,
-    uint32_t *__restrict__ vals_out, const uint32_t *__restrict__ counts,
-    const uint32_t *__restrict__ row_total, int64_t n, int64_t block_len, int num_blocks, int shift,
-    uint32_t mask)
-{
-    using Smem = WcSmem<K, PAIRS, WAVES, ITEMS, LE>;
-    constexpr int THREADS = Smem::kThreads;
-    constexpr int TILE = Smem::kTile;
-    constexpr int WAVE_KEYS = kWave * ITEMS;
-    constexpr int IPW = kWave / LE;  // lines per wave instruction
-    static_assert(THREADS >= kRadix, "one thread per digit is assumed");
-    static_assert(TILE <= 65536, "ranks are packed in 16 bits");
-    static_assert(LE == 8 || LE == 16 || LE == 32 || LE == 64, "a line is a power-of-two part of a wave");
-    static_assert(Smem::kMaxItems < 65536, "line indices");
-    __shared__ Smem s;
-
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
-    const int blk = blockIdx.x;
-    const int64_t blk_begin = (int64_t)blk * block_len;
-    const int64_t blk_end = blk_begin + block_len < n ? blk_begin + block_len : n;
-    const uint32_t n32 = (uint32_t)n;
-
-    if (wave == 0) {
-        const uint4 tot = reinterpret_cast<const uint4 *>(row_total)[lane];
-        const uint4 start = wave_scan_digits(tot);
-        const int d0 = 4 * lane;
-        uint4 r;
-        r.x = start.x + counts[(int64_t)(d0 + 0) * num_blocks + blk];
-        r.y = start.y + counts[(int64_t)(d0 + 1) * num_blocks + blk];
-        r.z = start.z + counts[(int64_t)(d0 + 2) * num_blocks + blk];
-        r.w = start.w + counts[(int64_t)(d0 + 3) * num_blocks + blk];
-        reinterpret_cast<uint4 *>(s.run)[lane] = r;
-        reinterpret_cast<uint4 *>(s.bstart)[lane] = r;
-    }
-
-    K cur[ITEMS];
-    {
-        const int valid0 = blk_end - blk_begin < TILE ? (int)(blk_end - blk_begin) : TILE;
-        issue_tile_loads<K, ITEMS>(cur, keys_in + blk_begin, wave * WAVE_KEYS + lane, valid0);
-    }
-
-    for (int64_t tile_begin = blk_begin; tile_begin < blk_end; tile_begin += TILE) {
-        const int valid = blk_end - tile_begin < TILE ? (int)(blk_end - tile_begin) : TILE;
-        const bool full = valid == TILE;
-        const bool last = tile_begin + TILE >= blk_end;
-        int tid_l = tid;
-        asm volatile("" : "+v"(tid_l));
-        const int first = (tid_l / kWave) * WAVE_KEYS + (tid_l & (kWave - 1));
-
-        K nxt[ITEMS];
-        const int64_t next_begin = tile_begin + TILE;
-        if (!last) {
-            const int nvalid = blk_end - next_begin < TILE ? (int)(blk_end - next_begin) : TILE;
-            issue_tile_loads<K, ITEMS>(nxt, keys_in + next_begin, first, nvalid);
-        }
-        uint32_t v[ITEMS];
-        if constexpr (PAIRS) issue_tile_loads<uint32_t, ITEMS>(v, vals_in + tile_begin, first, valid);
-        finish_tile<K, ENCODE, ITEMS>(cur, first, valid, full);
-
-        // Carry the previous tile's unfinished lines: its keys are still in
-        // LDS (this tile's keys overwrite them only after two barriers).  The
-        // previous tile was full and not the block's last.
-        if (tile_begin != blk_begin) {
-#pragma unroll
-            for (int i = 0; i < ITEMS; ++i) {
-                const uint32_t j = (uint32_t)(i * THREADS + tid_l);
-                const K x = s.keys[j];
-                const uint32_t d = digit_of(x, shift, mask);
-                const uint2 t = s.tail[d];
-                if (j >= t.x) {
-                    const uint32_t e = (j + t.y) & (uint32_t)(LE - 1);
-                    s.ckeys[d][e] = x;
-                    if constexpr (PAIRS) s.cvals[d][e] = s.vals[j];
-                }
-            }
-        }
-
-#pragma unroll
-        for (int j = 0; j < kRadix / kWave; ++j) s.wave_count[wave][lane + j * kWave] = 0u;
-
-        uint32_t r[ITEMS];
-#pragma unroll
-        for (int i = 0; i < ITEMS; ++i) {
-            const uint32_t d = digit_of(cur[i], shift, mask);
-            uint32_t *counter = &s.wave_count[wave][d];
-            const uint32_t prior = *counter;
-            uint32_t lo, hi;
-            match_digit(d, lo, hi);
-            const uint32_t below = lanes_below(lo, hi);
-            const uint32_t same = __popc(lo) + __popc(hi);
-            uint32_t *dst = (below + 1u == same) ? counter : &s.sink[wave][lane];
-            *dst = prior + same;
-            r[i] = (d << 16) | (prior + below);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        __syncthreads();
-
-        if (wave == 0) {
-            uint4 c[WAVES];
-            uint4 tot = make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll
-            for (int w = 0; w < WAVES; ++w) {
-                c[w] = reinterpret_cast<const uint4 *>(s.wave_count[w])[lane];
-                const uint4 e = tot;
-                tot.x += c[w].x; tot.y += c[w].y; tot.z += c[w].z; tot.w += c[w].w;
-                c[w] = e;
-            }
-            const uint4 off = wave_scan_digits(tot);
-#pragma unroll
-            for (int w = 0; w < WAVES; ++w) {
-                reinterpret_cast<uint4 *>(s.wave_count[w])[lane] =
-                    make_uint4(c[w].x + off.x, c[w].y + off.y, c[w].z + off.z, c[w].w + off.w);
-            }
-            const uint4 run = reinterpret_cast<const uint4 *>(s.run)[lane];
-            const uint4 bst = reinterpret_cast<const uint4 *>(s.bstart)[lane];
-            const uint32_t pad = (uint32_t)(TILE - valid);
-            const int d0 = 4 * lane;
-            const uint32_t cnt[4] = {tot.x, tot.y, tot.z, tot.w};
-            const uint32_t toff[4] = {off.x, off.y, off.z, off.w};
-            const uint32_t rb[4] = {run.x, run.y, run.z, run.w};
-            const uint32_t bs[4] = {bst.x, bst.y, bst.z, bst.w};
-            uint32_t items[4], hi[4], line0[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                // padding slots of a short last tile were counted under digit `mask`
-                const uint32_t real = cnt[k] - ((uint32_t)(d0 + k) == mask ? pad : 0u);
-                hi[k] = rb[k] + real;
-                const uint32_t lo = max(rb[k] & ~(uint32_t)(LE - 1), bs[k]);
-                line0[k] = lo & ~(uint32_t)(LE - 1);
-                if (last)
-                    items[k] = hi[k] > lo ? (hi[k] + LE - 1) / LE - lo / LE : 0u;
-                else
-                    items[k] = hi[k] / LE - lo / LE;
-            }
-            const uint4 ioff = wave_scan_digits(make_uint4(items[0], items[1], items[2], items[3]));
-            const uint32_t io[4] = {ioff.x, ioff.y, ioff.z, ioff.w};
-            uint4 inf[4];
-            uint2 tl[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                inf[k] = make_uint4(line0[k] - io[k] * (uint32_t)LE, rb[k], toff[k] - rb[k], hi[k]);
-                const uint32_t pend_from = max(hi[k] & ~(uint32_t)(LE - 1), rb[k]);
-                tl[k] = make_uint2(toff[k] + (pend_from - rb[k]), rb[k] - toff[k]);
-                for (uint32_t q = 0; q < items[k]; ++q) s.owner[io[k] + q] = (uint8_t)(d0 + k);
-            }
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                s.info[d0 + k] = inf[k];
-                s.tail[d0 + k] = tl[k];
-            }
-            reinterpret_cast<uint4 *>(s.run)[lane] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-            if (lane == kWave - 1) s.n_items = io[3] + items[3];
-        }
-        __syncthreads();
-
-#pragma unroll
-        for (int i = 0; i < ITEMS; ++i) r[i] = (r[i] & 0xFFFFu) + s.wave_count[wave][r[i] >> 16];
-#pragma unroll
-        for (int i = 0; i < ITEMS; ++i) {
-            s.keys[r[i]] = cur[i];
-            if constexpr (PAIRS) s.vals[r[i]] = v[i];
-        }
-        // The next tile's keys are used here, before any store of this tile
-        // is issued: waiting for them later would also wait for every store.
-        if (!last) {
-#pragma unroll
-            for (int i = 0; i < ITEMS; ++i) asm volatile("" : "+v"(nxt[i]));
-        }
-        __syncthreads();
-
-        // Store the complete lines: lane e of line group g writes output
-        // position base + q*LE + e of line q, taking the key from the carry
-        // (positions before this tile's first key of the digit) or the tile.
-        {
-            const uint32_t total = s.n_items;
-            const uint32_t g = (uint32_t)(tid_l & (kWave - 1)) / LE;
-            const uint32_t e = (uint32_t)(tid_l & (LE - 1));
-            for (uint32_t q0 = (uint32_t)(tid_l / kWave) * IPW; q0 < total; q0 += WAVES * IPW) {
-                const uint32_t q = q0 + g;
-                if (q < total) {
-                    const uint32_t d = s.owner[q];
-                    const uint4 f = s.info[d];
-                    const uint32_t p = f.x + q * (uint32_t)LE + e;
-                    if (p >= s.bstart[d] && p < f.w) {
-                        const bool from_carry = p < f.y;
-                        const uint32_t slot = p + f.z;
-                        const K *ksrc = from_carry ? &s.ckeys[d][e] : &s.keys[slot];
-                        K x = *ksrc;
-                        if constexpr (DECODE) x = (K)decode_f32((uint32_t)x);
-                        const uint32_t dest = min(p, n32 - 1u);
-                        keys_out[dest] = x;
-                        if constexpr (PAIRS) {
-                            const uint32_t *vsrc = from_carry ? &s.cvals[d][e] : &s.vals[slot];
-                            vals_out[dest] = *vsrc;
-                        }
-                    }
-                }
-            }
-        }
-        __syncthreads();
 
 #pragma unroll
         for (int i = 0; i < ITEMS; ++i) cur[i] = nxt[i];

@@ -264,47 +264,23 @@ hipError_t launch_scan(uint32_t *counts, uint32_t *rowtot, int blocks, hipStream
     });
 }
 
-// Output line length (elements) of the write-combining downsweep per key type:
-// 128-byte key lines; 0 selects the plain downsweep.
-template <typename K, bool PAIRS>
-constexpr int line_elems()
-{
-#ifdef LRS_LINE_U32
-    if constexpr (sizeof(K) == 4 && !PAIRS) return LRS_LINE_U32;
-#endif
-#ifdef LRS_LINE_U32P
-    if constexpr (sizeof(K) == 4 && PAIRS) return LRS_LINE_U32P;
-#endif
-#ifdef LRS_LINE_U64
-    if constexpr (sizeof(K) == 8) return LRS_LINE_U64;
-#endif
-    return 0;
-}
-
-// Tiles written out together by the plain downsweep: as many as fit in a
-// 64 KB budget of tile LDS (more would cut occupancy below two workgroups).
+// Tiles written out together by the plain downsweep, per key type: two for
+// 32-bit keys; one for 64-bit keys, whose two 32 KB tiles would leave room
+// for a single workgroup per CU.
 template <typename K, bool PAIRS>
 constexpr int sub_tiles()
 {
 #ifdef LRS_SUB
-    constexpr int want = LRS_SUB;
+    return LRS_SUB;
 #else
-    constexpr int want = 2;
+    return sizeof(K) == 4 ? 2 : 1;
 #endif
-    constexpr int tile_bytes = (sizeof(K) == 8 ? kWaves64 * 64 * kItems64 : kWaves32 * 64 * kItems32) *
-                               (int)(sizeof(K) + (PAIRS ? 4 : 0));
-    constexpr int fit = (64 * 1024) / tile_bytes;
-    return want < fit ? want : (fit > 0 ? fit : 1);
 }
 
 template <typename K, bool PAIRS, int WAVES, int ITEMS, bool ENCODE, bool DECODE>
 auto downsweep_fn()
 {
-    constexpr int LE = line_elems<K, PAIRS>();
-    if constexpr (LE > 0)
-        return downsweep_wc_kernel<K, PAIRS, WAVES, ITEMS, LE, ENCODE, DECODE>;
-    else
-        return downsweep_kernel<K, PAIRS, WAVES, ITEMS, sub_tiles<K, PAIRS>(), ENCODE, DECODE>;
+    return downsweep_kernel<K, PAIRS, WAVES, ITEMS, sub_tiles<K, PAIRS>(), ENCODE, DECODE>;
 }
 
 template <typename K, bool PAIRS, int WAVES, int ITEMS, bool ENCODE, bool DECODE>
