@@ -283,26 +283,46 @@ struct DownsweepSmem {
     uint16_t sink[WAVES][kWave];                        // stores of non-leader lanes land here
 };
 
-// Issues the loads of one tile's keys for this lane: item i is key
-// first + i*64 of the tile.  The loads are non-temporal: each key is read once
-// per kernel, and keeping the stream out of L2 leaves it to the scattered
-// output lines that are still being filled.  A full tile loads from the tile base plus a
-// per-item immediate offset; in the short last tile, indices past the last
-// valid key are clamped to it, so every load stays inside the input (finish_tile
-// overwrites those slots).  Nothing here waits for the loads.
-template <typename K, int ITEMS>
-__device__ __forceinline__ void issue_tile_loads(K (&k)[ITEMS], const K *__restrict__ tile, int first, int valid)
+// Buffer resource over `bytes` bytes from `base`: buffer loads through it at
+// byte offsets at or past `bytes` return zero without touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_over(const void *base, uint32_t bytes)
 {
-    if (valid >= ITEMS * kWave * (int)(blockDim.x / kWave)) {
+    // word 3: 32-bit data format, the setting for untyped loads on gfx9-family parts
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+constexpr int kNonTemporal = 2;  // cache-policy bit: streaming access
+
+template <typename K>
+__device__ __forceinline__ K buffer_load_nt(__amdgpu_buffer_rsrc_t r, uint32_t off);
+template <>
+__device__ __forceinline__ uint32_t buffer_load_nt<uint32_t>(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kNonTemporal);
+}
+template <>
+__device__ __forceinline__ uint64_t buffer_load_nt<uint64_t>(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kNonTemporal);
+    return ((uint64_t)v[1] << 32) | v[0];
+}
+
+// Issues the loads of one tile's keys (or values) for this lane: item i is
+// element first + i*64 of the tile, which starts `tile_off` elements into the
+// block that `r` covers.  The loads are non-temporal: each key is read once
+// per kernel, and keeping the stream out of L2 leaves it to the scattered
+// output lines that are still being filled.  Elements past the block's end
+// (a short last tile, or a tile past the end) read as zero from the buffer's
+// range check: there is no branch, so every call issues the same loads, and
+// finish_tile overwrites such slots where they are used.  Nothing here waits
+// for the loads.
+template <typename K, int ITEMS>
+__device__ __forceinline__ void issue_tile_loads(K (&k)[ITEMS], __amdgpu_buffer_rsrc_t r, uint32_t tile_off,
+                                                 int first)
+{
+    const uint32_t off = (tile_off + (uint32_t)first) * (uint32_t)sizeof(K);
 #pragma unroll
-        for (int i = 0; i < ITEMS; ++i)
-            k[i] = __builtin_nontemporal_load(&tile[(uint32_t)first + (uint32_t)(i * kWave)]);
-    } else {
-        const uint32_t last = (uint32_t)(valid - 1);
-#pragma unroll
-        for (int i = 0; i < ITEMS; ++i)
-            k[i] = __builtin_nontemporal_load(&tile[min((uint32_t)(first + i * kWave), last)]);
-    }
+    for (int i = 0; i < ITEMS; ++i) k[i] = buffer_load_nt<K>(r, off + (uint32_t)(i * kWave * sizeof(K)));
 }
 
 // Applies the float encoding (first pass) and gives slots past `valid`
@@ -325,12 +345,20 @@ __device__ __forceinline__ void finish_tile(K (&k)[ITEMS], int first, int valid,
 // Stable rank + scatter of block b's tiles for one digit.  Tile layout: wave w
 // owns keys [w*64*ITEMS, (w+1)*64*ITEMS) of the tile, item i of lane l is key
 // w*64*ITEMS + i*64 + l, so each load instruction reads 64 consecutive keys and
-// (item, lane) order is input order.  The next tile's keys are loaded into
-// registers while the current tile is ranked and written.
+// (item, lane) order is input order.
 //
-// SUB consecutive tiles are ranked and reordered into SUB LDS regions before
-// they are written out together.  A digit's runs from consecutive tiles are
-// adjacent in the output, so the output line they share is completed by two
+// Tiles are taken two at a time, A and B, in two register buffers: while A is
+// ranked, B's keys load into the second buffer, and while B is ranked, the next
+// A's keys load into the first.  Unrolled this way the buffers stay in fixed
+// registers across the loop, with no copy at the loop head of a buffer whose
+// loads may still be in flight, so each wait for a prefetch sits where it is
+// placed below: before the tile that uses it, and always before a flush's
+// stores (the memory counter is in order, so a wait issued after stores would
+// wait for the stores too).
+//
+// SUB (1 or 2) consecutive tiles are ranked and reordered into SUB LDS regions
+// before they are written out together.  A digit's runs from consecutive tiles
+// are adjacent in the output, so the output line they share is completed by two
 // stores issued back to back (merged in L2) instead of one tile apart: the
 // store stream behaves like runs SUB times longer, with the registers of one
 // tile.
@@ -338,7 +366,7 @@ template <typename K, bool PAIRS, int WAVES, int ITEMS, int SUB, bool ENCODE, bo
 __global__ __launch_bounds__(WAVES * kWave) void downsweep_kernel(
     const K *__restrict__ keys_in, K *__restrict__ keys_out, const uint32_t *__restrict__ vals_in,
     uint32_t *__restrict__ vals_out, const uint32_t *__restrict__ counts,
-    const uint32_t *__restrict__ row_total, int64_t n, int64_t block_len, int num_blocks, int shift,
+    const uint32_t *__restrict__ row_total, int64_t n, int64_t block_len, int count_cols, int split, int shift,
     uint32_t mask)
 {
     using Smem = DownsweepSmem<K, PAIRS, WAVES, ITEMS, SUB>;
@@ -347,6 +375,7 @@ __global__ __launch_bounds__(WAVES * kWave) void downsweep_kernel(
     constexpr int WAVE_KEYS = kWave * ITEMS;
     static_assert(THREADS >= kRadix, "one thread per digit is assumed");
     static_assert(TILE < 65536, "ranks and counters are 16-bit");
+    static_assert(SUB == 1 || SUB == 2, "one or two tiles per flush");
     __shared__ Smem s;
 
     const int tid = threadIdx.x;
@@ -355,52 +384,67 @@ __global__ __launch_bounds__(WAVES * kWave) void downsweep_kernel(
     const int blk = blockIdx.x;
     const int64_t blk_begin = (int64_t)blk * block_len;
     const int64_t blk_end = blk_begin + block_len < n ? blk_begin + block_len : n;
-    const int first = wave * WAVE_KEYS + lane;
     const uint32_t n32 = (uint32_t)n;
 
     if (wave == 0) {
         // digit starts (exclusive prefix of the row totals), plus this block's
-        // exclusive prefix within each digit's row
+        // exclusive prefix within each digit's row.  The upsweep counted each
+        // block as `split` consecutive sub-blocks (count_cols columns in all),
+        // so the block's prefix is the one of its first sub-block.
         const uint4 tot = reinterpret_cast<const uint4 *>(row_total)[lane];
         const uint4 start = wave_scan_digits(tot);
         const int d0 = 4 * lane;
+        const int64_t col = (int64_t)blk * split;
         uint4 r;
-        r.x = start.x + counts[(int64_t)(d0 + 0) * num_blocks + blk];
-        r.y = start.y + counts[(int64_t)(d0 + 1) * num_blocks + blk];
-        r.z = start.z + counts[(int64_t)(d0 + 2) * num_blocks + blk];
-        r.w = start.w + counts[(int64_t)(d0 + 3) * num_blocks + blk];
+        r.x = start.x + counts[(int64_t)(d0 + 0) * count_cols + col];
+        r.y = start.y + counts[(int64_t)(d0 + 1) * count_cols + col];
+        r.z = start.z + counts[(int64_t)(d0 + 2) * count_cols + col];
+        r.w = start.w + counts[(int64_t)(d0 + 3) * count_cols + col];
         reinterpret_cast<uint4 *>(s.run)[lane] = r;
     }
 
-    K cur[ITEMS];
-    {
-        const int valid0 = blk_end - blk_begin < TILE ? (int)(blk_end - blk_begin) : TILE;
-        issue_tile_loads<K, ITEMS>(cur, keys_in + blk_begin, first, valid0);
-    }
+    // Makes the compiler wait here for a buffer's loads.
+    auto ready = [](K(&kb)[ITEMS]) {
+#pragma unroll
+        for (int i = 0; i < ITEMS; ++i) asm volatile("" : "+v"(kb[i]));
+    };
 
-    int sub = 0;  // region of this tile within the current group of SUB tiles
-    for (int64_t tile_begin = blk_begin; tile_begin < blk_end; tile_begin += TILE) {
-        const int valid = blk_end - tile_begin < TILE ? (int)(blk_end - tile_begin) : TILE;
-        const bool full = valid == TILE;
-        const bool last = tile_begin + TILE >= blk_end;
-        // Lane indices re-derived from an opaque copy each tile: the per-item
-        // offsets built from them then fold into the instructions that use
-        // them instead of being hoisted out of the loop into ~50 registers.
+    // Lane's first key in a tile.  Re-derived from an opaque copy of the lane
+    // index at each use: the per-item offsets built from it then fold into
+    // the instructions that use them instead of being hoisted out of the loop
+    // into ~50 registers.
+    auto lane_first = [&]() {
         int tid_l = tid;
         asm volatile("" : "+v"(tid_l));
-        const int first = (tid_l / kWave) * WAVE_KEYS + (tid_l & (kWave - 1));
+        return (tid_l / kWave) * WAVE_KEYS + (tid_l & (kWave - 1));
+    };
 
-        // Prefetch the next tile of the block; its loads are in flight while
-        // this tile is ranked and written.
-        K nxt[ITEMS];
-        const int64_t next_begin = tile_begin + TILE;
-        if (!last) {
-            const int nvalid = blk_end - next_begin < TILE ? (int)(blk_end - next_begin) : TILE;
-            issue_tile_loads<K, ITEMS>(nxt, keys_in + next_begin, first, nvalid);
-        }
+    // The block's keys and values, as buffers: loads past the block's end
+    // read zero.  A block holds at most 2^31 bytes of keys (the host keeps
+    // blocks below that).
+    const __amdgpu_buffer_rsrc_t keys_buf =
+        buffer_over(keys_in + blk_begin, (uint32_t)((blk_end - blk_begin) * (int64_t)sizeof(K)));
+    const __amdgpu_buffer_rsrc_t vals_buf =
+        buffer_over(PAIRS ? vals_in + blk_begin : nullptr, PAIRS ? (uint32_t)((blk_end - blk_begin) * 4) : 0u);
+
+    // Issues the loads of the block's tile at tile_begin into kb.  The same
+    // loads are issued whether or not the tile exists (past the block's end
+    // they read zero and move no data): every path then has the same count of
+    // memory operations in flight, so the compiler's wait counts stay exact
+    // instead of falling back to waits that also cover the stores.
+    auto prefetch = [&](K(&kb)[ITEMS], int64_t tile_begin) {
+        issue_tile_loads<K, ITEMS>(kb, keys_buf, (uint32_t)(tile_begin - blk_begin), lane_first());
+    };
+
+    // Ranks the tile at tile_begin, whose keys are in kb, into LDS region
+    // `sub`.  `par` selects the counter buffer (tile parity in the block).
+    auto rank_tile = [&](K(&kb)[ITEMS], int64_t tile_begin, int sub, int par) {
+        const int valid = blk_end - tile_begin < TILE ? (int)(blk_end - tile_begin) : TILE;
+        const bool full = valid == TILE;
+        const int first = lane_first();
         uint32_t v[ITEMS];
-        if constexpr (PAIRS) issue_tile_loads<uint32_t, ITEMS>(v, vals_in + tile_begin, first, valid);
-        finish_tile<K, ENCODE, ITEMS>(cur, first, valid, full);
+        if constexpr (PAIRS) issue_tile_loads<uint32_t, ITEMS>(v, vals_buf, (uint32_t)(tile_begin - blk_begin), first);
+        finish_tile<K, ENCODE, ITEMS>(kb, first, valid, full);
 
         // This wave's digit counters start at zero for the tile.  Counters
         // alternate between two buffers by tile parity: the other waves read
@@ -408,7 +452,6 @@ __global__ __launch_bounds__(WAVES * kWave) void downsweep_kernel(
         // cleared was last read by other waves in the tile before the
         // previous one (finished before the previous barrier) and by this
         // wave itself, as slot bases, in the previous tile.
-        const int par = (int)(((tile_begin - blk_begin) / TILE) & 1);
         uint16_t(&count)[WAVES][kRadix] = s.wave_count[par];
         uint16_t(&slot_base)[WAVES][kRadix] = s.wave_count[par ^ 1];
         reinterpret_cast<uint2 *>(count[wave])[lane] = make_uint2(0u, 0u);
@@ -423,7 +466,7 @@ __global__ __launch_bounds__(WAVES * kWave) void downsweep_kernel(
         uint32_t r[ITEMS];
 #pragma unroll
         for (int i = 0; i < ITEMS; ++i) {
-            const uint32_t d = digit_of(cur[i], shift, mask);
+            const uint32_t d = digit_of(kb[i], shift, mask);
             uint16_t *counter = &count[wave][d];
             const uint32_t prior = *counter;
             uint32_t lo, hi;
@@ -474,63 +517,104 @@ __global__ __launch_bounds__(WAVES * kWave) void downsweep_kernel(
         for (int i = 0; i < ITEMS; ++i) r[i] = (r[i] & 0xFFFFu) + slot_base[wave][r[i] >> 16];
 #pragma unroll
         for (int i = 0; i < ITEMS; ++i) {
-            s.keys[sub][r[i]] = cur[i];
+            s.keys[sub][r[i]] = kb[i];
             if constexpr (PAIRS) s.vals[sub][r[i]] = v[i];
         }
+    };
 
-        if (sub == SUB - 1 || last) {
-            // The next tile's keys are used here, before any store is issued:
-            // waiting for them after the stores would wait for the stores too.
-            if (!last) {
+    // Writes LDS region t, a full tile, to the output.  Consecutive threads
+    // take consecutive slots: each digit's run of slots goes to consecutive
+    // global addresses.  With matching counts in upsweep and downsweep every
+    // dest is below n; the clamp here (and the test in the short tile) only
+    // keeps a key array changed between the two kernels by a racing caller
+    // from turning into stores outside the output.  No barrier follows: the
+    // LDS read here is next written after the next tile's rank barrier.
+    auto store_full = [&](int t) {
+        int tid_l = tid;
+        asm volatile("" : "+v"(tid_l));
 #pragma unroll
-                for (int i = 0; i < ITEMS; ++i) asm volatile("" : "+v"(nxt[i]));
-            }
-            __syncthreads();
-
-            // Consecutive threads take consecutive slots: each digit's run of
-            // slots goes to consecutive global addresses.  With matching counts
-            // in upsweep and downsweep every dest is below n; the clamp (full
-            // tiles) and the test (short tile) only keep a key array changed
-            // between the two kernels by a racing caller from turning into
-            // stores outside the output.  Only the block's last tile can be
-            // short.  No barrier follows: the LDS read here is next written
-            // after the next tile's rank barrier.
-            for (int t = 0; t <= sub; ++t) {
-                if (!last || t < sub || full) {
+        for (int i = 0; i < ITEMS; ++i) {
+            const uint32_t j = (uint32_t)(i * THREADS + tid_l);
+            const K x = s.keys[t][j];
+            const uint32_t dest = min(s.out_base[t][digit_of(x, shift, mask)] + j, n32 - 1u);
+            K y = x;
+            if constexpr (DECODE) y = (K)decode_f32((uint32_t)x);
+            keys_out[dest] = y;
+            if constexpr (PAIRS) vals_out[dest] = s.vals[t][j];
+        }
+    };
+    // Region t holding the block's last tile, with `valid` keys.
+    auto store_last = [&](int t, int valid) {
+        int tid_l = tid;
+        asm volatile("" : "+v"(tid_l));
 #pragma unroll
-                    for (int i = 0; i < ITEMS; ++i) {
-                        const uint32_t j = (uint32_t)(i * THREADS + tid_l);
-                        const K x = s.keys[t][j];
-                        const uint32_t dest = min(s.out_base[t][digit_of(x, shift, mask)] + j, n32 - 1u);
-                        K y = x;
-                        if constexpr (DECODE) y = (K)decode_f32((uint32_t)x);
-                        keys_out[dest] = y;
-                        if constexpr (PAIRS) vals_out[dest] = s.vals[t][j];
-                    }
-                } else {
-#pragma unroll
-                    for (int i = 0; i < ITEMS; ++i) {
-                        const int j = i * THREADS + tid_l;
-                        if (j < valid) {
-                            const K x = s.keys[t][j];
-                            const uint32_t dest = s.out_base[t][digit_of(x, shift, mask)] + (uint32_t)j;
-                            K y = x;
-                            if constexpr (DECODE) y = (K)decode_f32((uint32_t)x);
-                            if (dest < n32) {
-                                keys_out[dest] = y;
-                                if constexpr (PAIRS) vals_out[dest] = s.vals[t][j];
-                            }
-                        }
-                    }
+        for (int i = 0; i < ITEMS; ++i) {
+            const int j = i * THREADS + tid_l;
+            if (j < valid) {
+                const K x = s.keys[t][j];
+                const uint32_t dest = s.out_base[t][digit_of(x, shift, mask)] + (uint32_t)j;
+                K y = x;
+                if constexpr (DECODE) y = (K)decode_f32((uint32_t)x);
+                if (dest < n32) {
+                    keys_out[dest] = y;
+                    if constexpr (PAIRS) vals_out[dest] = s.vals[t][j];
                 }
             }
-            sub = 0;
-        } else {
-            ++sub;
         }
+    };
 
+    // Tile t's keys are loaded two tiles ahead: the loads are issued as soon
+    // as tile t-2 has been moved to LDS, before tile t-2's stores.  The memory
+    // counter is in order, so waiting for those keys (at tile t) never waits
+    // for stores issued after them; stores drain while the next tiles rank.
+    // The first two tiles load B before A and wait for both, so that on entry
+    // to the loop neither buffer is in flight, and the loop has one exit and
+    // the same memory operations on every path: each wait below is counted
+    // exactly, not conservatively.  A wave keeps at most 63 memory operations
+    // in flight, so A's loads are issued only after B's keys have arrived:
+    // then no wait covers more than the stores.
+    K a[ITEMS], b[ITEMS];
+    prefetch(b, blk_begin + TILE);
+    prefetch(a, blk_begin);
+    ready(a);
+
+    // Tiles go in pairs, A in buffer a and B in buffer b.  The loop takes the
+    // pairs before the block's last tile; the last one or two tiles (the last
+    // may be short) follow it.
+    const int tiles = (int)((blk_end - blk_begin + TILE - 1) / TILE);
+    const int pairs = (tiles - 1) / 2;
+    int64_t ta = blk_begin;
+    for (int p = 0; p < pairs; ++p, ta += 2 * TILE) {
+        const int64_t tb = ta + TILE;
+        rank_tile(a, ta, 0, 0);
+        if constexpr (SUB == 1) {
+            __syncthreads();
+            store_full(0);
+        }
+        ready(b);
+        prefetch(a, ta + 2 * TILE);
+        rank_tile(b, tb, SUB - 1, 1);
+        prefetch(b, tb + 2 * TILE);
+        __syncthreads();
 #pragma unroll
-        for (int i = 0; i < ITEMS; ++i) cur[i] = nxt[i];
+        for (int t = 0; t < SUB; ++t) store_full(t);
+        ready(a);
+    }
+
+    rank_tile(a, ta, 0, 0);
+    if (tiles - 2 * pairs == 1) {
+        __syncthreads();
+        store_last(0, (int)(blk_end - ta));
+    } else {
+        if constexpr (SUB == 1) {
+            __syncthreads();
+            store_full(0);
+        }
+        ready(b);
+        rank_tile(b, ta + TILE, SUB - 1, 1);
+        __syncthreads();
+        if constexpr (SUB == 2) store_full(0);
+        store_last(SUB - 1, (int)(blk_end - ta - TILE));
     }
 }
 

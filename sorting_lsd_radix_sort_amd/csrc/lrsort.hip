@@ -18,6 +18,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <map>
 #include <mutex>
 #include <vector>
 
@@ -34,14 +35,18 @@ using namespace lrs;
 enum KeyKind { KIND_U32 = 0, KIND_F32 = 1, KIND_U64 = 2 };
 
 constexpr int kMaxBlocks = 4096;  // count-matrix width cap (scan: 256 threads x 16)
+constexpr int kMaxSplit = 8;      // upsweep sub-blocks per downsweep block
 constexpr int kUpsweepThreads = 512;
 constexpr int kScanThreads = 256;
 constexpr int kScanPerThread = kMaxBlocks / kScanThreads;
 constexpr size_t kAlign = 256;
 
-// Downsweep tile shapes (waves per workgroup x keys per lane).
-constexpr int kWaves32 = 4, kItems32 = 16;  // 4096-key tiles for 32-bit keys
-constexpr int kWaves64 = 4, kItems64 = 16;  // 4096-key tiles for 64-bit keys
+// Downsweep tile shapes (waves per workgroup x keys per lane): 8192-key
+// tiles.  The tile size sets how many keys of each digit a workgroup writes
+// in one piece (about tile/256 per tile): longer pieces leave fewer
+// partly-written 128-byte lines, which cost HBM bandwidth.
+constexpr int kWaves32 = 8, kItems32 = 16;
+constexpr int kWaves64 = 8, kItems64 = 16;
 
 int tile_keys(KeyKind kind) { return kind == KIND_U64 ? kWaves64 * 64 * kItems64 : kWaves32 * 64 * kItems32; }
 
@@ -100,24 +105,25 @@ hipError_t device_cus(int *cus)
     return hipSuccess;
 }
 
-// Resident workgroups per CU of a kernel (cached per kernel and device).
-template <typename Kern>
-hipError_t occupancy(Kern kern, int threads, int *per_cu)
+// Resident workgroups per CU of a kernel, cached per kernel and device.  The
+// cache is keyed by the kernel's address: kernels of one signature (keys only
+// and pairs, say) share a function type but not an occupancy.
+hipError_t occupancy(const void *kern, int threads, int *per_cu)
 {
     static std::mutex mu;
-    static int cache[64] = {0};
+    static std::map<std::pair<int, const void *>, int> cache;
     int dev = 0;
     hipError_t err = hipGetDevice(&dev);
     if (err != hipSuccess) return err;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
     std::lock_guard<std::mutex> lock(mu);
-    if (cache[dev] == 0) {
+    auto it = cache.find({dev, kern});
+    if (it == cache.end()) {
         int nb = 0;
         err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, threads, 0);
         if (err != hipSuccess) return err;
-        cache[dev] = nb > 0 ? nb : 1;
+        it = cache.emplace(std::make_pair(dev, kern), nb > 0 ? nb : 1).first;
     }
-    *per_cu = cache[dev];
+    *per_cu = it->second;
     return hipSuccess;
 }
 
@@ -177,7 +183,7 @@ struct Layout {
     int passes = 0;
     int tile = 0;
     int64_t tiles = 0;
-    int max_blocks = 0;
+    int max_cols = 0;  // count-matrix columns (upsweep sub-blocks) at most
     Plan kplan, vplan;
     size_t off_counts = 0, off_rowtot = 0, off_ka = 0, off_kb = 0, off_va = 0, off_vb = 0;
     size_t total = 0;
@@ -190,12 +196,12 @@ Layout make_layout(const Request &rq)
     L.passes = (rq.end_bit - rq.begin_bit + kRadixBits - 1) / kRadixBits;
     L.tile = tile_keys(rq.kind);
     L.tiles = (rq.n + L.tile - 1) / L.tile;
-    L.max_blocks = (int)std::min<int64_t>(L.tiles, kMaxBlocks);
+    L.max_cols = (int)std::min<int64_t>(L.tiles * kMaxSplit, kMaxBlocks);
     L.kplan = make_plan(L.passes, rq.keys_in == rq.keys_out);
     L.vplan = make_plan(L.passes, rq.vals_in != nullptr && rq.vals_in == rq.vals_out);
     size_t off = 0;
     L.off_counts = off;
-    off += align_up((size_t)kRadix * L.max_blocks * 4);
+    off += align_up((size_t)kRadix * L.max_cols * 4);
     L.off_rowtot = off;
     off += align_up((size_t)kRadix * 4);
     const size_t kbytes = align_up((size_t)rq.n * ksz), vbytes = align_up((size_t)rq.n * 4);
@@ -264,9 +270,9 @@ hipError_t launch_scan(uint32_t *counts, uint32_t *rowtot, int blocks, hipStream
     });
 }
 
-// Tiles written out together by the plain downsweep, per key type: two for
-// 32-bit keys; one for 64-bit keys, whose two 32 KB tiles would leave room
-// for a single workgroup per CU.
+// Tiles written out together by the downsweep, per key type: two for 32-bit
+// keys (76 KB of LDS for keys only, two workgroups per CU); one for 64-bit
+// keys, whose tile alone takes 64 KB.
 template <typename K, bool PAIRS>
 constexpr int sub_tiles()
 {
@@ -285,33 +291,34 @@ auto downsweep_fn()
 
 template <typename K, bool PAIRS, int WAVES, int ITEMS, bool ENCODE, bool DECODE>
 hipError_t launch_downsweep(const K *kin, K *kout, const uint32_t *vin, uint32_t *vout, const uint32_t *counts,
-                            const uint32_t *rowtot, int64_t n, int64_t block_len, int blocks, int shift,
-                            uint32_t mask, hipStream_t stream)
+                            const uint32_t *rowtot, int64_t n, int64_t block_len, int blocks, int cols, int split,
+                            int shift, uint32_t mask, hipStream_t stream)
 {
     return launch(LRS_KERNEL_DOWNSWEEP, stream, [&] {
         downsweep_fn<K, PAIRS, WAVES, ITEMS, ENCODE, DECODE>()<<<blocks, WAVES * 64, 0, stream>>>(
-            kin, kout, vin, vout, counts, rowtot, n, block_len, blocks, shift, mask);
+            kin, kout, vin, vout, counts, rowtot, n, block_len, cols, split, shift, mask);
     });
 }
 
 template <typename K, bool PAIRS, int WAVES, int ITEMS>
 hipError_t downsweep_dispatch(bool enc, bool dec, const K *kin, K *kout, const uint32_t *vin, uint32_t *vout,
                               const uint32_t *counts, const uint32_t *rowtot, int64_t n, int64_t block_len,
-                              int blocks, int shift, uint32_t mask, hipStream_t stream)
+                              int blocks, int cols, int split, int shift, uint32_t mask, hipStream_t stream)
 {
     if constexpr (sizeof(K) == 4) {
         if (enc && dec)
             return launch_downsweep<K, PAIRS, WAVES, ITEMS, true, true>(kin, kout, vin, vout, counts, rowtot, n,
-                                                                         block_len, blocks, shift, mask, stream);
+                                                                         block_len, blocks, cols, split, shift,
+                                                                         mask, stream);
         if (enc)
             return launch_downsweep<K, PAIRS, WAVES, ITEMS, true, false>(kin, kout, vin, vout, counts, rowtot, n,
-                                                                          block_len, blocks, shift, mask, stream);
+                                                                          block_len, blocks, cols, split, shift, mask, stream);
         if (dec)
             return launch_downsweep<K, PAIRS, WAVES, ITEMS, false, true>(kin, kout, vin, vout, counts, rowtot, n,
-                                                                          block_len, blocks, shift, mask, stream);
+                                                                          block_len, blocks, cols, split, shift, mask, stream);
     }
     return launch_downsweep<K, PAIRS, WAVES, ITEMS, false, false>(kin, kout, vin, vout, counts, rowtot, n,
-                                                                   block_len, blocks, shift, mask, stream);
+                                                                   block_len, blocks, cols, split, shift, mask, stream);
 }
 
 // The kernel whose occupancy sets the number of blocks for this key type.
@@ -321,9 +328,14 @@ hipError_t blocks_for(int64_t tiles, int *blocks)
     int cus = 0, per_cu = 0;
     hipError_t err = device_cus(&cus);
     if (err != hipSuccess) return err;
-    err = occupancy(downsweep_fn<K, PAIRS, WAVES, ITEMS, false, false>(), WAVES * 64, &per_cu);
+    err = occupancy((const void *)downsweep_fn<K, PAIRS, WAVES, ITEMS, false, false>(), WAVES * 64, &per_cu);
     if (err != hipSuccess) return err;
-    const int64_t want = std::max<int64_t>(1, (int64_t)cus * per_cu);
+    // The downsweep reads a block's keys through a buffer whose size field is
+    // 32-bit: keep every block below 2^30 bytes (at least 32 blocks at the
+    // largest n of 64-bit keys, well inside the count-matrix width).
+    constexpr int64_t kMaxBlockTiles = ((int64_t)1 << 30) / ((int64_t)WAVES * 64 * ITEMS * (int64_t)sizeof(K));
+    const int64_t want = std::max<int64_t>(std::max<int64_t>(1, (int64_t)cus * per_cu),
+                                           (tiles + kMaxBlockTiles - 1) / kMaxBlockTiles);
     *blocks = (int)std::min<int64_t>(std::min<int64_t>(tiles, want), kMaxBlocks);
     return hipSuccess;
 }
@@ -337,6 +349,20 @@ lrs_status run_passes(const Request &rq, const Layout &L, char *temp, hipStream_
     const int64_t tiles_per_block = (L.tiles + want_blocks - 1) / want_blocks;
     const int64_t block_len = tiles_per_block * TILE;
     const int blocks = (int)((rq.n + block_len - 1) / block_len);
+    // The upsweep counts each block as `split` sub-blocks, so that it runs as
+    // many workgroups as fill the chip however few blocks the downsweep's
+    // occupancy allows; the count matrix has one column per sub-block.
+    int cus = 0, up_per_cu = 0;
+    if (device_cus(&cus) != hipSuccess) return LRS_ERR_HIP;
+    if (occupancy((const void *)upsweep_kernel<K, false, kUpsweepThreads, true>, kUpsweepThreads, &up_per_cu) !=
+        hipSuccess)
+        return LRS_ERR_HIP;
+    int split = 1;
+    while (split < kMaxSplit && (int64_t)blocks * split * 2 <= kMaxBlocks &&
+           (int64_t)blocks * split < (int64_t)cus * up_per_cu)
+        split *= 2;
+    const int64_t sub_len = block_len / split;  // TILE is a multiple of kMaxSplit
+    const int cols = (int)((rq.n + sub_len - 1) / sub_len);
 
     uint32_t *counts = (uint32_t *)(temp + L.off_counts);
     uint32_t *rowtot = (uint32_t *)(temp + L.off_rowtot);
@@ -360,20 +386,18 @@ lrs_status run_passes(const Request &rq, const Layout &L, char *temp, hipStream_
         hipError_t err;
         if constexpr (sizeof(K) == 4) {
             if (enc)
-                err = launch_upsweep<K, true>(kbuf_const[ksrc], counts, rq.n, block_len, blocks, shift, mask,
-                                              stream);
+                err = launch_upsweep<K, true>(kbuf_const[ksrc], counts, rq.n, sub_len, cols, shift, mask, stream);
             else
-                err = launch_upsweep<K, false>(kbuf_const[ksrc], counts, rq.n, block_len, blocks, shift, mask,
-                                               stream);
+                err = launch_upsweep<K, false>(kbuf_const[ksrc], counts, rq.n, sub_len, cols, shift, mask, stream);
         } else {
-            err = launch_upsweep<K, false>(kbuf_const[ksrc], counts, rq.n, block_len, blocks, shift, mask, stream);
+            err = launch_upsweep<K, false>(kbuf_const[ksrc], counts, rq.n, sub_len, cols, shift, mask, stream);
         }
         if (err != hipSuccess) return LRS_ERR_HIP;
-        if (launch_scan(counts, rowtot, blocks, stream) != hipSuccess) return LRS_ERR_HIP;
+        if (launch_scan(counts, rowtot, cols, stream) != hipSuccess) return LRS_ERR_HIP;
         err = downsweep_dispatch<K, PAIRS, WAVES, ITEMS>(enc, dec, kbuf_const[ksrc], kbuf[kdst],
                                                          PAIRS ? vbuf_const[vsrc] : nullptr,
                                                          PAIRS ? vbuf[vdst] : nullptr, counts, rowtot, rq.n,
-                                                         block_len, blocks, shift, mask, stream);
+                                                         block_len, blocks, cols, split, shift, mask, stream);
         if (err != hipSuccess) return LRS_ERR_HIP;
         ksrc = kdst;
         vsrc = vdst;

@@ -24,8 +24,9 @@ from sorting_lsd_radix_sort_amd import inputs
 
 pytestmark = pytest.mark.gpu
 
-TILE = 4096
-SMALL_SIZES = [0, 1, 2, 3, 63, 64, 65, 255, 256, 257, TILE - 1, TILE, TILE + 1, 3 * TILE + 17, 65_536]
+TILE = 8192  # keys per downsweep tile
+SMALL_SIZES = [0, 1, 2, 3, 63, 64, 65, 255, 256, 257, 1023, 1024, 1025, 4095, 4096, 4097,
+               TILE - 1, TILE, TILE + 1, 2 * TILE, 3 * TILE + 17, 65_536]
 RANGES = {"u32": [(0, 32), (0, 20), (8, 16), (3, 17), (31, 32), (24, 32), (5, 5)],
           "f32": [(0, 32), (0, 20), (16, 32), (31, 32)],
           "u64": [(0, 64), (0, 40), (32, 64), (5, 61), (63, 64)]}
