@@ -110,7 +110,7 @@ def main() -> int:
     kout = torch.empty_like(kin)
     vin = torch.from_numpy(vals_np).to(dev) if vals_np is not None else None
     vout = torch.empty_like(vin) if vin is not None else None
-    sfx = {"u32": "u32", "f32": "f32", "u64": "u64"}[cfg.key_type]
+    sfx = cfg.key_type
     if vin is None:
         fn = getattr(lrs, "lrs_sort_keys_" + sfx)
         arrays = (kin, kout)
@@ -144,25 +144,24 @@ def main() -> int:
     gkeys = n / (ms_per_step * 1e-3) / 1e9
 
     # ---- sanity check of the last output (ordered, same multiset sum)
-    if cfg.key_type == "f32":
-        ko = kout.view(torch.int32)
-        f = kout
-        ordered = bool((f[1:] >= f[:-1]).all().item())
-        same_sum = bool(torch.equal(kin.view(torch.int32).to(torch.int64).sum(), ko.to(torch.int64).sum()))
-    else:
-        width = 64 if cfg.key_type == "u64" else 32
-        as_i = kout.view(torch.int64 if width == 64 else torch.int32)
+    width = 8 * ksz
+    as_i = kout.view(torch.int64 if width == 64 else torch.int32)
+    src_i = kin.view(as_i.dtype)
+    same_sum = bool(torch.equal((src_i.to(torch.int64) & 0xFFFF).sum(), (as_i.to(torch.int64) & 0xFFFF).sum()))
+    full = cfg.begin_bit == 0 and cfg.end_bit == width
+    if cfg.key_type in ("f32", "f64", "i32", "i64") and full:
+        ordered = bool((kout[1:] >= kout[:-1]).all().item())  # NaN-free inputs
+    elif width == 32 and cfg.key_type == "u32":
         mask = (1 << (cfg.end_bit - cfg.begin_bit)) - 1
-        if width == 32:
-            w = (as_i.to(torch.int64) & 0xFFFFFFFF) >> cfg.begin_bit
-            w = w & mask
-            ordered = bool((w[1:] >= w[:-1]).all().item())
-        else:
-            hi = (as_i >> 32) & 0xFFFFFFFF
-            lo = as_i & 0xFFFFFFFF
-            ordered = bool(((hi[1:] > hi[:-1]) | ((hi[1:] == hi[:-1]) & (lo[1:] >= lo[:-1]))).all().item())
-        src_i = kin.view(as_i.dtype)
-        same_sum = bool(torch.equal((src_i.to(torch.int64) & 0xFFFF).sum(), (as_i.to(torch.int64) & 0xFFFF).sum()))
+        w = ((as_i.to(torch.int64) & 0xFFFFFFFF) >> cfg.begin_bit) & mask
+        ordered = bool((w[1:] >= w[:-1]).all().item())
+    elif width == 64 and cfg.key_type == "u64" and full:
+        hi = (as_i >> 32) & 0xFFFFFFFF
+        lo = as_i & 0xFFFFFFFF
+        ordered = bool(((hi[1:] > hi[:-1]) | ((hi[1:] == hi[:-1]) & (lo[1:] >= lo[:-1]))).all().item())
+    else:
+        raise SystemExit("bench.py has no output check for %s over bits [%d,%d)"
+                         % (cfg.key_type, cfg.begin_bit, cfg.end_bit))
     if vout is not None:
         same_sum = same_sum and int(vout.to(torch.int64).sum().item()) == n * (n - 1) // 2
     log("[bench] output ordered=%s multiset-sum=%s" % (ordered, same_sum))

@@ -16,12 +16,17 @@
  * Keys and values move together in one sort, never as a key sort followed by a
  * gather (same page, section 5.5).
  *
- * Float32 keys are ordered through the sign-flip encoding of the kwkr.cn essay
- * on bitonic vs. LSD radix sort, section 3.3 (non-negative floats: set the sign
- * bit; negative floats: invert every bit), applied on the first load and undone
- * on the last store; for them [begin_bit, end_bit) indexes the encoded word.
- * Under it -0.0 sorts before +0.0, +NaN after +inf and -NaN before -inf; bit
- * patterns come back unchanged.
+ * Key types.  Every key type is ordered as an unsigned word, the key's order
+ * code, and [begin_bit, end_bit) indexes that word:
+ *  - u32, u64: the key itself;
+ *  - i32, i64 (two's complement): the key with its sign bit flipped (the page
+ *    "GPU radix sort ...", section 5.2), so negative keys sort first;
+ *  - f32, f64 (IEEE-754): non-negative floats get the sign bit set, negative
+ *    floats get every bit inverted (same page, section 5.3; the kwkr.cn essay
+ *    on bitonic vs. LSD radix sort, section 3.3).  Under it -0.0 sorts before
+ *    +0.0, +NaN after +inf and -NaN before -inf.
+ * The code is formed in registers to pick each digit; keys are stored and
+ * returned as the caller's bit patterns, unchanged.
  *
  * Conventions shared by every sort call:
  *  - Two-phase temp storage (same page, section 2, and section 6, first
@@ -79,6 +84,15 @@ lrs_status lrs_sort_keys_u64(void *d_temp, size_t *temp_bytes,
 lrs_status lrs_sort_keys_f32(void *d_temp, size_t *temp_bytes,
                              const float *d_keys_in, float *d_keys_out,
                              int64_t n, int begin_bit, int end_bit, hipStream_t stream);
+lrs_status lrs_sort_keys_i32(void *d_temp, size_t *temp_bytes,
+                             const int32_t *d_keys_in, int32_t *d_keys_out,
+                             int64_t n, int begin_bit, int end_bit, hipStream_t stream);
+lrs_status lrs_sort_keys_i64(void *d_temp, size_t *temp_bytes,
+                             const int64_t *d_keys_in, int64_t *d_keys_out,
+                             int64_t n, int begin_bit, int end_bit, hipStream_t stream);
+lrs_status lrs_sort_keys_f64(void *d_temp, size_t *temp_bytes,
+                             const double *d_keys_in, double *d_keys_out,
+                             int64_t n, int begin_bit, int end_bit, hipStream_t stream);
 
 /* Pair sorts: (d_keys_in[i], d_values_in[i]) move together to the outputs.
  * Argument order follows the pair call of the page "GPU radix sort ...",
@@ -94,6 +108,18 @@ lrs_status lrs_sort_pairs_u64(void *d_temp, size_t *temp_bytes,
 lrs_status lrs_sort_pairs_f32(void *d_temp, size_t *temp_bytes,
                               const float *d_keys_in, const uint32_t *d_values_in,
                               float *d_keys_out, uint32_t *d_values_out,
+                              int64_t n, int begin_bit, int end_bit, hipStream_t stream);
+lrs_status lrs_sort_pairs_i32(void *d_temp, size_t *temp_bytes,
+                              const int32_t *d_keys_in, const uint32_t *d_values_in,
+                              int32_t *d_keys_out, uint32_t *d_values_out,
+                              int64_t n, int begin_bit, int end_bit, hipStream_t stream);
+lrs_status lrs_sort_pairs_i64(void *d_temp, size_t *temp_bytes,
+                              const int64_t *d_keys_in, const uint32_t *d_values_in,
+                              int64_t *d_keys_out, uint32_t *d_values_out,
+                              int64_t n, int begin_bit, int end_bit, hipStream_t stream);
+lrs_status lrs_sort_pairs_f64(void *d_temp, size_t *temp_bytes,
+                              const double *d_keys_in, const uint32_t *d_values_in,
+                              double *d_keys_out, uint32_t *d_values_out,
                               int64_t n, int begin_bit, int end_bit, hipStream_t stream);
 
 /* Static description of a status code (never NULL). */

@@ -7,8 +7,8 @@ never import it, and it imports nothing from them.
 The arithmetic lives in ``lsd_oracle.c`` (plain C, one thread): the serial LSD
 loop of the kwkr.cn essay on bitonic vs. LSD radix sort, section 3.1, with the
 half-open bit range of the page "GPU radix sort: from the CUB implementation to
-performance tuning", section 2, and the float32 sign-flip encoding of the essay's
-section 3.3.  This module only builds that file with gcc and marshals numpy
+performance tuning", section 2, the float sign-flip encoding of the essay's
+section 3.3 and the signed-integer sign flip of the page's section 5.2.  This module only builds that file with gcc and marshals numpy
 arrays into it.
 """
 from __future__ import annotations
@@ -23,10 +23,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "lsd_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-KIND_U32, KIND_F32, KIND_U64 = 0, 1, 2
+KIND_U32, KIND_F32, KIND_U64, KIND_I32, KIND_I64, KIND_F64 = 0, 1, 2, 3, 4, 5
 _KIND_OF_DTYPE = {np.dtype(np.uint32): KIND_U32, np.dtype(np.float32): KIND_F32,
-                  np.dtype(np.uint64): KIND_U64}
-_KEY_BITS = {KIND_U32: 32, KIND_F32: 32, KIND_U64: 64}
+                  np.dtype(np.uint64): KIND_U64, np.dtype(np.int32): KIND_I32,
+                  np.dtype(np.int64): KIND_I64, np.dtype(np.float64): KIND_F64}
+_KEY_BITS = {KIND_U32: 32, KIND_F32: 32, KIND_U64: 64, KIND_I32: 32, KIND_I64: 64, KIND_F64: 64}
 
 _lib = None
 
@@ -51,10 +52,17 @@ def _load():
         lib.oracle_f2s.restype = ctypes.c_uint32
         lib.oracle_s2f.argtypes = [ctypes.c_uint32]
         lib.oracle_s2f.restype = ctypes.c_uint32
+        for name, t in (("oracle_i32_code", ctypes.c_uint32), ("oracle_i64_code", ctypes.c_uint64),
+                        ("oracle_f64_code", ctypes.c_uint64), ("oracle_f64_uncode", ctypes.c_uint64)):
+            fn = getattr(lib, name)
+            fn.argtypes = [t]
+            fn.restype = t
         for name in ("oracle_f2s_array", "oracle_s2f_array"):
             fn = getattr(lib, name)
             fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64]
             fn.restype = None
+        lib.oracle_code_array.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64]
+        lib.oracle_code_array.restype = ctypes.c_int
         lib.oracle_sort.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                     ctypes.c_int, ctypes.c_int]
@@ -88,11 +96,44 @@ def s2f(words) -> np.ndarray:
     return out
 
 
+def order_code(bits, kind: int) -> int:
+    """The oracle's order-preserving word of one key's bit pattern (an int)."""
+    lib = _load()
+    if kind == KIND_F32:
+        return int(lib.oracle_f2s(int(bits)))
+    if kind == KIND_I32:
+        return int(lib.oracle_i32_code(int(bits)))
+    if kind == KIND_I64:
+        return int(lib.oracle_i64_code(int(bits)))
+    if kind == KIND_F64:
+        return int(lib.oracle_f64_code(int(bits)))
+    return int(bits)
+
+
+def order_codes(keys: np.ndarray) -> np.ndarray:
+    """The oracle's order-preserving words of an array of keys, as uint64."""
+    k = np.ascontiguousarray(keys).reshape(-1)
+    kind = _KIND_OF_DTYPE.get(k.dtype)
+    if kind is None:
+        raise TypeError("no order code for %s" % k.dtype)
+    out = np.empty(k.size, dtype=np.uint64)
+    rc = _load().oracle_code_array(kind, _ptr(k), _ptr(out), k.size)
+    if rc:
+        raise ValueError("oracle_code_array failed with code %d" % rc)
+    return out
+
+
+def f64_uncode(word: int) -> int:
+    """Inverse of the float64 order code (an int in, an int out)."""
+    return int(_load().oracle_f64_uncode(int(word)))
+
+
 def _prepare(keys, values, begin_bit, end_bit):
     keys = np.ascontiguousarray(keys)
     kind = _KIND_OF_DTYPE.get(keys.dtype)
     if kind is None:
-        raise TypeError("oracle keys must be uint32, float32 or uint64, got %s" % keys.dtype)
+        raise TypeError("oracle keys must be uint32, int32, float32, uint64, int64 or float64, "
+                        "got %s" % keys.dtype)
     if end_bit is None:
         end_bit = _KEY_BITS[kind]
     if values is not None:

@@ -58,6 +58,34 @@ uint32_t oracle_s2f(uint32_t u)
     return (u & 0x80000000u) ? (u ^ 0x80000000u) : ~u;
 }
 
+/* Signed keys (two's complement) -> order-preserving unsigned words: flip
+ * the sign bit (page "GPU radix sort ...", section 5.2: the most negative
+ * value becomes 0, the most positive all ones).  Flipping twice restores the
+ * key, so the same function is its own inverse. */
+uint32_t oracle_i32_code(uint32_t bits)
+{
+    return bits ^ 0x80000000u;
+}
+
+uint64_t oracle_i64_code(uint64_t bits)
+{
+    return bits ^ 0x8000000000000000ull;
+}
+
+/* Float64 -> order-preserving uint64: the float32 rule above on the 64-bit
+ * pattern (sign clear: set the sign bit; sign set: invert every bit), and its
+ * reverse mapping. */
+uint64_t oracle_f64_code(uint64_t bits)
+{
+    uint64_t mask = (bits & 0x8000000000000000ull) ? 0xFFFFFFFFFFFFFFFFull : 0x8000000000000000ull;
+    return bits ^ mask;
+}
+
+uint64_t oracle_f64_uncode(uint64_t u)
+{
+    return (u & 0x8000000000000000ull) ? (u ^ 0x8000000000000000ull) : ~u;
+}
+
 void oracle_f2s_array(const uint32_t *in, uint32_t *out, int64_t n)
 {
     for (int64_t i = 0; i < n; ++i) out[i] = oracle_f2s(in[i]);
@@ -140,14 +168,57 @@ static int check_args(int64_t n, int begin_bit, int end_bit, int key_bits)
     return ORACLE_OK;
 }
 
-/* key_kind: 0 = uint32, 1 = float32 (sorted through oracle_f2s), 2 = uint64.
- * keys_in/keys_out hold raw bit patterns (4 or 8 bytes per key).  vals_in and
+/* Key kinds: 0 = uint32, 1 = float32, 2 = uint64, 3 = int32, 4 = int64,
+ * 5 = float64.  Each kind is sorted by its order-preserving unsigned word
+ * (the identity, or one of the codes above) and written back through the
+ * inverse, so keys come out as the caller's bit patterns. */
+static int kind_bits(int key_kind)
+{
+    return (key_kind == 2 || key_kind == 4 || key_kind == 5) ? 64 : 32;
+}
+
+static uint64_t to_word(int key_kind, uint64_t raw)
+{
+    switch (key_kind) {
+    case 1: return oracle_f2s((uint32_t)raw);
+    case 3: return oracle_i32_code((uint32_t)raw);
+    case 4: return oracle_i64_code(raw);
+    case 5: return oracle_f64_code(raw);
+    default: return raw;
+    }
+}
+
+static uint64_t from_word(int key_kind, uint64_t w)
+{
+    switch (key_kind) {
+    case 1: return oracle_s2f((uint32_t)w);
+    case 3: return oracle_i32_code((uint32_t)w);
+    case 4: return oracle_i64_code(w);
+    case 5: return oracle_f64_uncode(w);
+    default: return w;
+    }
+}
+
+/* The order-preserving words of n keys of the given kind (as uint64). */
+int oracle_code_array(int key_kind, const void *keys, uint64_t *words, int64_t n)
+{
+    if (key_kind < 0 || key_kind > 5 || n < 0) return ORACLE_ERR_ARG;
+    for (int64_t i = 0; i < n; ++i) {
+        uint64_t raw = kind_bits(key_kind) == 64 ? ((const uint64_t *)keys)[i]
+                                                 : ((const uint32_t *)keys)[i];
+        words[i] = to_word(key_kind, raw);
+    }
+    return ORACLE_OK;
+}
+
+/* keys_in/keys_out hold raw bit patterns (4 or 8 bytes per key).  vals_in and
  * vals_out are both NULL for a keys-only sort.  Inputs are never modified. */
 int oracle_sort(int key_kind, const void *keys_in, const uint32_t *vals_in,
                 void *keys_out, uint32_t *vals_out, int64_t n,
                 int begin_bit, int end_bit)
 {
-    int key_bits = key_kind == 2 ? 64 : 32;
+    if (key_kind < 0 || key_kind > 5) return ORACLE_ERR_ARG;
+    int key_bits = kind_bits(key_kind);
     int rc = check_args(n, begin_bit, end_bit, key_bits);
     if (rc) return rc;
     if ((vals_in == NULL) != (vals_out == NULL)) return ORACLE_ERR_ARG;
@@ -162,23 +233,23 @@ int oracle_sort(int key_kind, const void *keys_in, const uint32_t *vals_in,
         memcpy(vals, vals_in, (size_t)n * sizeof(uint32_t));
     }
 
-    if (key_kind == 2) {
-        memcpy(words, keys_in, (size_t)n * sizeof(uint64_t));
+    if (key_bits == 64) {
+        const uint64_t *k64 = (const uint64_t *)keys_in;
+        for (int64_t i = 0; i < n; ++i) words[i] = to_word(key_kind, k64[i]);
     } else {
         const uint32_t *k32 = (const uint32_t *)keys_in;
-        for (int64_t i = 0; i < n; ++i)
-            words[i] = key_kind == 1 ? oracle_f2s(k32[i]) : k32[i];
+        for (int64_t i = 0; i < n; ++i) words[i] = to_word(key_kind, k32[i]);
     }
 
     rc = lsd_sort_words(words, vals, n, begin_bit, end_bit);
 
     if (rc == ORACLE_OK) {
-        if (key_kind == 2) {
-            memcpy(keys_out, words, (size_t)n * sizeof(uint64_t));
+        if (key_bits == 64) {
+            uint64_t *o64 = (uint64_t *)keys_out;
+            for (int64_t i = 0; i < n; ++i) o64[i] = from_word(key_kind, words[i]);
         } else {
             uint32_t *o32 = (uint32_t *)keys_out;
-            for (int64_t i = 0; i < n; ++i)
-                o32[i] = key_kind == 1 ? oracle_s2f((uint32_t)words[i]) : (uint32_t)words[i];
+            for (int64_t i = 0; i < n; ++i) o32[i] = (uint32_t)from_word(key_kind, words[i]);
         }
         if (vals_out) memcpy(vals_out, vals, (size_t)n * sizeof(uint32_t));
     }

@@ -25,8 +25,8 @@ LRS_ERR_HIP = 3
 
 KERNEL_NAMES = {0: "upsweep", 1: "scan", 2: "downsweep", 3: "copy"}
 
-SORT_FUNCTIONS = ("lrs_sort_keys_u32", "lrs_sort_keys_u64", "lrs_sort_keys_f32",
-                  "lrs_sort_pairs_u32", "lrs_sort_pairs_u64", "lrs_sort_pairs_f32")
+KEY_TYPES = ("u32", "i32", "f32", "u64", "i64", "f64")
+SORT_FUNCTIONS = tuple("lrs_sort_keys_" + t for t in KEY_TYPES) + tuple("lrs_sort_pairs_" + t for t in KEY_TYPES)
 EXPORTED = SORT_FUNCTIONS + ("lrs_status_string", "lrs_device_copy", "lrs_prof_start",
                              "lrs_prof_stop", "lrs_prof_count", "lrs_prof_read",
                              "lrs_prof_release")
@@ -145,11 +145,17 @@ def _make_pairs(name):
 
 
 lrs_sort_keys_u32 = _make_keys("lrs_sort_keys_u32")
-lrs_sort_keys_u64 = _make_keys("lrs_sort_keys_u64")
+lrs_sort_keys_i32 = _make_keys("lrs_sort_keys_i32")
 lrs_sort_keys_f32 = _make_keys("lrs_sort_keys_f32")
+lrs_sort_keys_u64 = _make_keys("lrs_sort_keys_u64")
+lrs_sort_keys_i64 = _make_keys("lrs_sort_keys_i64")
+lrs_sort_keys_f64 = _make_keys("lrs_sort_keys_f64")
 lrs_sort_pairs_u32 = _make_pairs("lrs_sort_pairs_u32")
-lrs_sort_pairs_u64 = _make_pairs("lrs_sort_pairs_u64")
+lrs_sort_pairs_i32 = _make_pairs("lrs_sort_pairs_i32")
 lrs_sort_pairs_f32 = _make_pairs("lrs_sort_pairs_f32")
+lrs_sort_pairs_u64 = _make_pairs("lrs_sort_pairs_u64")
+lrs_sort_pairs_i64 = _make_pairs("lrs_sort_pairs_i64")
+lrs_sort_pairs_f64 = _make_pairs("lrs_sort_pairs_f64")
 
 
 def lrs_device_copy(d_dst, d_src, nbytes: int, stream=None) -> None:
@@ -184,15 +190,17 @@ def lrs_prof_release() -> None:
 
 # ------------------------------------------------------------- conveniences
 
-_KEY_SUFFIX = {"torch.uint32": "u32", "torch.uint64": "u64", "torch.float32": "f32"}
-KEY_BITS = {"u32": 32, "u64": 64, "f32": 32}
+_KEY_SUFFIX = {"torch.uint32": "u32", "torch.int32": "i32", "torch.float32": "f32",
+               "torch.uint64": "u64", "torch.int64": "i64", "torch.float64": "f64"}
+KEY_BITS = {"u32": 32, "i32": 32, "f32": 32, "u64": 64, "i64": 64, "f64": 64}
 
 
 def key_suffix(dtype) -> str:
     try:
         return _KEY_SUFFIX[str(dtype)]
     except KeyError:
-        raise TypeError("lrsort sorts uint32, uint64 or float32 keys, not %s" % dtype) from None
+        raise TypeError("lrsort sorts keys of type uint32, int32, float32, uint64, int64 or "
+                        "float64, not %s" % dtype) from None
 
 
 def _temp_tensor(nbytes, device, temp):
@@ -203,8 +211,9 @@ def _temp_tensor(nbytes, device, temp):
 
 
 def sort_keys(keys, begin_bit: int = 0, end_bit: int | None = None, out=None, temp=None, stream=None):
-    """Stable ascending sort of a 1-D device tensor of uint32/uint64/float32 keys
-    over bits [begin_bit, end_bit); returns the output tensor."""
+    """Stable ascending sort of a 1-D device tensor of keys (uint32, int32,
+    float32, uint64, int64 or float64) over bits [begin_bit, end_bit) of their
+    order code; returns the output tensor."""
     import torch
     sfx = key_suffix(keys.dtype)
     end_bit = KEY_BITS[sfx] if end_bit is None else end_bit

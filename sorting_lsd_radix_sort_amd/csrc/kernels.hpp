@@ -34,6 +34,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace lrs {
 
 constexpr int kRadixBits = 8;
@@ -43,24 +45,47 @@ constexpr int kWave = 64;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // ------------------------------------------------------------------ key codes
+//
+// Keys stay as the caller gave them, in every buffer and every pass.  A pass
+// orders keys by a digit of an order-preserving unsigned code of the key,
+// formed in registers only to take that digit (the codes are those of the page
+// "GPU radix sort: from the CUB implementation to performance tuning",
+// sections 5.2-5.3, and of the kwkr.cn essay on bitonic vs. LSD radix sort,
+// section 3.3):
+//   unsigned   the key itself;
+//   signed     two's complement with the sign bit flipped;
+//   float      IEEE-754: sign clear -> sign bit set; sign set -> all bits
+//              inverted (so -0.0 orders just below +0.0 and NaNs past the
+//              infinities of their sign).
+enum KeyCode { CODE_UNSIGNED = 0, CODE_SIGNED = 1, CODE_FLOAT = 2 };
 
-// Float32 bit pattern -> order-preserving unsigned word (kwkr.cn essay,
-// section 3.3): sign clear -> set the sign bit; sign set -> invert all bits.
-__device__ __forceinline__ uint32_t encode_f32(uint32_t b)
+template <typename K, int CODE>
+__device__ __forceinline__ K order_code(K k)
 {
-    return b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);
+    constexpr int kTop = 8 * (int)sizeof(K) - 1;
+    constexpr K kSign = (K)1 << kTop;
+    using S = typename std::conditional<sizeof(K) == 4, int32_t, int64_t>::type;
+    if constexpr (CODE == CODE_SIGNED) {
+        return k ^ kSign;
+    } else if constexpr (CODE == CODE_FLOAT) {
+        return k ^ ((K)((S)k >> kTop) | kSign);  // arithmetic shift: all ones if negative
+    } else {
+        return k;
+    }
 }
 
-// Inverse of encode_f32: top bit set -> clear it; top bit clear -> invert all.
-__device__ __forceinline__ uint32_t decode_f32(uint32_t u)
-{
-    return u ^ (~(uint32_t)((int32_t)u >> 31) | 0x80000000u);
-}
-
-template <typename K>
+template <int CODE, typename K>
 __device__ __forceinline__ uint32_t digit_of(K k, int shift, uint32_t mask)
 {
-    return (uint32_t)(k >> shift) & mask;
+    return (uint32_t)(order_code<K, CODE>(k) >> shift) & mask;
+}
+
+// A key whose code is all ones: its digit is the largest of any pass, so the
+// padding slots of a short tile rank after every real key.
+template <typename K, int CODE>
+__device__ __forceinline__ K pad_key()
+{
+    return CODE == CODE_UNSIGNED ? ~(K)0 : (K)(~(K)0 >> 1);  // 0x7f..f: sign clear, code all ones
 }
 
 // --------------------------------------------------------------- wave helpers
@@ -162,7 +187,7 @@ __device__ __forceinline__ uint4 wave_scan_digits(uint4 c)
 // within a wave (the kwkr.cn essay, section 3.2, and the quant67.com survey,
 // section 8.1: per-block and per-warp counting instead of global atomics).
 // VEC loads 16 bytes per lane when the key array is 16-byte aligned.
-template <typename K, bool ENCODE, int THREADS, bool VEC>
+template <typename K, int CODE, int THREADS, bool VEC>
 __global__ __launch_bounds__(THREADS) void upsweep_kernel(
     const K *__restrict__ keys, uint32_t *__restrict__ counts, int64_t n, int64_t block_len,
     int num_blocks, int shift, uint32_t mask)
@@ -183,8 +208,7 @@ __global__ __launch_bounds__(THREADS) void upsweep_kernel(
     const int64_t end = begin + block_len < n ? begin + block_len : n;
 
     auto count_key = [&](K k) {
-        if constexpr (ENCODE) k = (K)encode_f32((uint32_t)k);
-        atomicAdd(&h[digit_of(k, shift, mask)], 1u);
+        atomicAdd(&h[digit_of<CODE>(k, shift, mask)], 1u);
     };
 
     int64_t scalar_from = begin;
@@ -325,20 +349,15 @@ __device__ __forceinline__ void issue_tile_loads(K (&k)[ITEMS], __amdgpu_buffer_
     for (int i = 0; i < ITEMS; ++i) k[i] = buffer_load_nt<K>(r, off + (uint32_t)(i * kWave * sizeof(K)));
 }
 
-// Applies the float encoding (first pass) and gives slots past `valid`
-// all-ones, i.e. the largest digit of any pass, so they rank after every real
-// key of the tile.
-template <typename K, bool ENCODE, int ITEMS>
+// Gives slots past `valid` the padding key, whose digit is the largest of any
+// pass, so they rank after every real key of the tile.
+template <typename K, int CODE, int ITEMS>
 __device__ __forceinline__ void finish_tile(K (&k)[ITEMS], int first, int valid, bool full)
 {
-#pragma unroll
-    for (int i = 0; i < ITEMS; ++i) {
-        if constexpr (ENCODE) k[i] = (K)encode_f32((uint32_t)k[i]);
-    }
     if (!full) {
 #pragma unroll
         for (int i = 0; i < ITEMS; ++i)
-            if (first + i * kWave >= valid) k[i] = ~(K)0;
+            if (first + i * kWave >= valid) k[i] = pad_key<K, CODE>();
     }
 }
 
@@ -362,7 +381,7 @@ __device__ __forceinline__ void finish_tile(K (&k)[ITEMS], int first, int valid,
 // stores issued back to back (merged in L2) instead of one tile apart: the
 // store stream behaves like runs SUB times longer, with the registers of one
 // tile.
-template <typename K, bool PAIRS, int WAVES, int ITEMS, int SUB, bool ENCODE, bool DECODE>
+template <typename K, bool PAIRS, int WAVES, int ITEMS, int SUB, int CODE>
 __global__ __launch_bounds__(WAVES * kWave) void downsweep_kernel(
     const K *__restrict__ keys_in, K *__restrict__ keys_out, const uint32_t *__restrict__ vals_in,
     uint32_t *__restrict__ vals_out, const uint32_t *__restrict__ counts,
@@ -444,7 +463,7 @@ __global__ __launch_bounds__(WAVES * kWave) void downsweep_kernel(
         const int first = lane_first();
         uint32_t v[ITEMS];
         if constexpr (PAIRS) issue_tile_loads<uint32_t, ITEMS>(v, vals_buf, (uint32_t)(tile_begin - blk_begin), first);
-        finish_tile<K, ENCODE, ITEMS>(kb, first, valid, full);
+        finish_tile<K, CODE, ITEMS>(kb, first, valid, full);
 
         // This wave's digit counters start at zero for the tile.  Counters
         // alternate between two buffers by tile parity: the other waves read
@@ -466,7 +485,7 @@ __global__ __launch_bounds__(WAVES * kWave) void downsweep_kernel(
         uint32_t r[ITEMS];
 #pragma unroll
         for (int i = 0; i < ITEMS; ++i) {
-            const uint32_t d = digit_of(kb[i], shift, mask);
+            const uint32_t d = digit_of<CODE>(kb[i], shift, mask);
             uint16_t *counter = &count[wave][d];
             const uint32_t prior = *counter;
             uint32_t lo, hi;
@@ -536,10 +555,8 @@ __global__ __launch_bounds__(WAVES * kWave) void downsweep_kernel(
         for (int i = 0; i < ITEMS; ++i) {
             const uint32_t j = (uint32_t)(i * THREADS + tid_l);
             const K x = s.keys[t][j];
-            const uint32_t dest = min(s.out_base[t][digit_of(x, shift, mask)] + j, n32 - 1u);
-            K y = x;
-            if constexpr (DECODE) y = (K)decode_f32((uint32_t)x);
-            keys_out[dest] = y;
+            const uint32_t dest = min(s.out_base[t][digit_of<CODE>(x, shift, mask)] + j, n32 - 1u);
+            keys_out[dest] = x;
             if constexpr (PAIRS) vals_out[dest] = s.vals[t][j];
         }
     };
@@ -552,11 +569,9 @@ __global__ __launch_bounds__(WAVES * kWave) void downsweep_kernel(
             const int j = i * THREADS + tid_l;
             if (j < valid) {
                 const K x = s.keys[t][j];
-                const uint32_t dest = s.out_base[t][digit_of(x, shift, mask)] + (uint32_t)j;
-                K y = x;
-                if constexpr (DECODE) y = (K)decode_f32((uint32_t)x);
+                const uint32_t dest = s.out_base[t][digit_of<CODE>(x, shift, mask)] + (uint32_t)j;
                 if (dest < n32) {
-                    keys_out[dest] = y;
+                    keys_out[dest] = x;
                     if constexpr (PAIRS) vals_out[dest] = s.vals[t][j];
                 }
             }

@@ -32,7 +32,13 @@ namespace {
 
 using namespace lrs;
 
-enum KeyKind { KIND_U32 = 0, KIND_F32 = 1, KIND_U64 = 2 };
+// Key types: storage width and order code (see order_code in kernels.hpp).
+enum KeyKind { KIND_U32, KIND_I32, KIND_F32, KIND_U64, KIND_I64, KIND_F64 };
+int key_bytes(KeyKind k) { return k == KIND_U64 || k == KIND_I64 || k == KIND_F64 ? 8 : 4; }
+int key_code(KeyKind k)
+{
+    return k == KIND_I32 || k == KIND_I64 ? CODE_SIGNED : k == KIND_F32 || k == KIND_F64 ? CODE_FLOAT : CODE_UNSIGNED;
+}
 
 constexpr int kMaxBlocks = 4096;  // count-matrix width cap (scan: 256 threads x 16)
 constexpr int kMaxSplit = 8;      // upsweep sub-blocks per downsweep block
@@ -48,7 +54,7 @@ constexpr size_t kAlign = 256;
 constexpr int kWaves32 = 8, kItems32 = 16;
 constexpr int kWaves64 = 8, kItems64 = 16;
 
-int tile_keys(KeyKind kind) { return kind == KIND_U64 ? kWaves64 * 64 * kItems64 : kWaves32 * 64 * kItems32; }
+int tile_keys(KeyKind kind) { return key_bytes(kind) == 8 ? kWaves64 * 64 * kItems64 : kWaves32 * 64 * kItems32; }
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -192,7 +198,7 @@ struct Layout {
 Layout make_layout(const Request &rq)
 {
     Layout L;
-    const size_t ksz = rq.kind == KIND_U64 ? 8 : 4;
+    const size_t ksz = (size_t)key_bytes(rq.kind);
     L.passes = (rq.end_bit - rq.begin_bit + kRadixBits - 1) / kRadixBits;
     L.tile = tile_keys(rq.kind);
     L.tiles = (rq.n + L.tile - 1) / L.tile;
@@ -248,17 +254,17 @@ lrs_status copy_bytes(void *dst, const void *src, size_t bytes, hipStream_t stre
 
 // ------------------------------------------------------------ pass launchers
 
-template <typename K, bool ENCODE>
+template <typename K, int CODE>
 hipError_t launch_upsweep(const K *keys, uint32_t *counts, int64_t n, int64_t block_len, int blocks, int shift,
                           uint32_t mask, hipStream_t stream)
 {
     const bool vec = ((uintptr_t)keys % 16) == 0;
     return launch(LRS_KERNEL_UPSWEEP, stream, [&] {
         if (vec)
-            upsweep_kernel<K, ENCODE, kUpsweepThreads, true>
+            upsweep_kernel<K, CODE, kUpsweepThreads, true>
                 <<<blocks, kUpsweepThreads, 0, stream>>>(keys, counts, n, block_len, blocks, shift, mask);
         else
-            upsweep_kernel<K, ENCODE, kUpsweepThreads, false>
+            upsweep_kernel<K, CODE, kUpsweepThreads, false>
                 <<<blocks, kUpsweepThreads, 0, stream>>>(keys, counts, n, block_len, blocks, shift, mask);
     });
 }
@@ -283,52 +289,31 @@ constexpr int sub_tiles()
 #endif
 }
 
-template <typename K, bool PAIRS, int WAVES, int ITEMS, bool ENCODE, bool DECODE>
+template <typename K, bool PAIRS, int WAVES, int ITEMS, int CODE>
 auto downsweep_fn()
 {
-    return downsweep_kernel<K, PAIRS, WAVES, ITEMS, sub_tiles<K, PAIRS>(), ENCODE, DECODE>;
+    return downsweep_kernel<K, PAIRS, WAVES, ITEMS, sub_tiles<K, PAIRS>(), CODE>;
 }
 
-template <typename K, bool PAIRS, int WAVES, int ITEMS, bool ENCODE, bool DECODE>
+template <typename K, bool PAIRS, int WAVES, int ITEMS, int CODE>
 hipError_t launch_downsweep(const K *kin, K *kout, const uint32_t *vin, uint32_t *vout, const uint32_t *counts,
                             const uint32_t *rowtot, int64_t n, int64_t block_len, int blocks, int cols, int split,
                             int shift, uint32_t mask, hipStream_t stream)
 {
     return launch(LRS_KERNEL_DOWNSWEEP, stream, [&] {
-        downsweep_fn<K, PAIRS, WAVES, ITEMS, ENCODE, DECODE>()<<<blocks, WAVES * 64, 0, stream>>>(
+        downsweep_fn<K, PAIRS, WAVES, ITEMS, CODE>()<<<blocks, WAVES * 64, 0, stream>>>(
             kin, kout, vin, vout, counts, rowtot, n, block_len, cols, split, shift, mask);
     });
 }
 
-template <typename K, bool PAIRS, int WAVES, int ITEMS>
-hipError_t downsweep_dispatch(bool enc, bool dec, const K *kin, K *kout, const uint32_t *vin, uint32_t *vout,
-                              const uint32_t *counts, const uint32_t *rowtot, int64_t n, int64_t block_len,
-                              int blocks, int cols, int split, int shift, uint32_t mask, hipStream_t stream)
-{
-    if constexpr (sizeof(K) == 4) {
-        if (enc && dec)
-            return launch_downsweep<K, PAIRS, WAVES, ITEMS, true, true>(kin, kout, vin, vout, counts, rowtot, n,
-                                                                         block_len, blocks, cols, split, shift,
-                                                                         mask, stream);
-        if (enc)
-            return launch_downsweep<K, PAIRS, WAVES, ITEMS, true, false>(kin, kout, vin, vout, counts, rowtot, n,
-                                                                          block_len, blocks, cols, split, shift, mask, stream);
-        if (dec)
-            return launch_downsweep<K, PAIRS, WAVES, ITEMS, false, true>(kin, kout, vin, vout, counts, rowtot, n,
-                                                                          block_len, blocks, cols, split, shift, mask, stream);
-    }
-    return launch_downsweep<K, PAIRS, WAVES, ITEMS, false, false>(kin, kout, vin, vout, counts, rowtot, n,
-                                                                   block_len, blocks, cols, split, shift, mask, stream);
-}
-
 // The kernel whose occupancy sets the number of blocks for this key type.
-template <typename K, bool PAIRS, int WAVES, int ITEMS>
+template <typename K, bool PAIRS, int WAVES, int ITEMS, int CODE>
 hipError_t blocks_for(int64_t tiles, int *blocks)
 {
     int cus = 0, per_cu = 0;
     hipError_t err = device_cus(&cus);
     if (err != hipSuccess) return err;
-    err = occupancy((const void *)downsweep_fn<K, PAIRS, WAVES, ITEMS, false, false>(), WAVES * 64, &per_cu);
+    err = occupancy((const void *)downsweep_fn<K, PAIRS, WAVES, ITEMS, CODE>(), WAVES * 64, &per_cu);
     if (err != hipSuccess) return err;
     // The downsweep reads a block's keys through a buffer whose size field is
     // 32-bit: keep every block below 2^30 bytes (at least 32 blocks at the
@@ -340,12 +325,12 @@ hipError_t blocks_for(int64_t tiles, int *blocks)
     return hipSuccess;
 }
 
-template <typename K, bool PAIRS, int WAVES, int ITEMS>
+template <typename K, bool PAIRS, int WAVES, int ITEMS, int CODE>
 lrs_status run_passes(const Request &rq, const Layout &L, char *temp, hipStream_t stream)
 {
     constexpr int TILE = WAVES * 64 * ITEMS;
     int want_blocks = 0;
-    if (blocks_for<K, PAIRS, WAVES, ITEMS>(L.tiles, &want_blocks) != hipSuccess) return LRS_ERR_HIP;
+    if (blocks_for<K, PAIRS, WAVES, ITEMS, CODE>(L.tiles, &want_blocks) != hipSuccess) return LRS_ERR_HIP;
     const int64_t tiles_per_block = (L.tiles + want_blocks - 1) / want_blocks;
     const int64_t block_len = tiles_per_block * TILE;
     const int blocks = (int)((rq.n + block_len - 1) / block_len);
@@ -354,7 +339,7 @@ lrs_status run_passes(const Request &rq, const Layout &L, char *temp, hipStream_
     // occupancy allows; the count matrix has one column per sub-block.
     int cus = 0, up_per_cu = 0;
     if (device_cus(&cus) != hipSuccess) return LRS_ERR_HIP;
-    if (occupancy((const void *)upsweep_kernel<K, false, kUpsweepThreads, true>, kUpsweepThreads, &up_per_cu) !=
+    if (occupancy((const void *)upsweep_kernel<K, CODE, kUpsweepThreads, true>, kUpsweepThreads, &up_per_cu) !=
         hipSuccess)
         return LRS_ERR_HIP;
     int split = 1;
@@ -373,31 +358,20 @@ lrs_status run_passes(const Request &rq, const Layout &L, char *temp, hipStream_
                                      (const uint32_t *)(temp + L.off_vb)};
     uint32_t *vbuf[4] = {nullptr, rq.vals_out, (uint32_t *)(temp + L.off_va), (uint32_t *)(temp + L.off_vb)};
 
-    const bool is_f32 = rq.kind == KIND_F32;
     int ksrc = BUF_IN, vsrc = BUF_IN;
     for (int p = 0; p < L.passes; ++p) {
         const int shift = rq.begin_bit + kRadixBits * p;
         const int width = std::min(kRadixBits, rq.end_bit - shift);
         const uint32_t mask = (1u << width) - 1u;
-        const bool enc = is_f32 && p == 0;
-        const bool dec = is_f32 && p == L.passes - 1;
         const int kdst = L.kplan.dst[p], vdst = L.vplan.dst[p];
 
-        hipError_t err;
-        if constexpr (sizeof(K) == 4) {
-            if (enc)
-                err = launch_upsweep<K, true>(kbuf_const[ksrc], counts, rq.n, sub_len, cols, shift, mask, stream);
-            else
-                err = launch_upsweep<K, false>(kbuf_const[ksrc], counts, rq.n, sub_len, cols, shift, mask, stream);
-        } else {
-            err = launch_upsweep<K, false>(kbuf_const[ksrc], counts, rq.n, sub_len, cols, shift, mask, stream);
-        }
+        hipError_t err = launch_upsweep<K, CODE>(kbuf_const[ksrc], counts, rq.n, sub_len, cols, shift, mask, stream);
         if (err != hipSuccess) return LRS_ERR_HIP;
         if (launch_scan(counts, rowtot, cols, stream) != hipSuccess) return LRS_ERR_HIP;
-        err = downsweep_dispatch<K, PAIRS, WAVES, ITEMS>(enc, dec, kbuf_const[ksrc], kbuf[kdst],
-                                                         PAIRS ? vbuf_const[vsrc] : nullptr,
-                                                         PAIRS ? vbuf[vdst] : nullptr, counts, rowtot, rq.n,
-                                                         block_len, blocks, cols, split, shift, mask, stream);
+        err = launch_downsweep<K, PAIRS, WAVES, ITEMS, CODE>(kbuf_const[ksrc], kbuf[kdst],
+                                                             PAIRS ? vbuf_const[vsrc] : nullptr,
+                                                             PAIRS ? vbuf[vdst] : nullptr, counts, rowtot, rq.n,
+                                                             block_len, blocks, cols, split, shift, mask, stream);
         if (err != hipSuccess) return LRS_ERR_HIP;
         ksrc = kdst;
         vsrc = vdst;
@@ -414,11 +388,20 @@ lrs_status run_passes(const Request &rq, const Layout &L, char *temp, hipStream_
     return LRS_OK;
 }
 
+template <typename K, int CODE>
+lrs_status run_kind(bool pairs, const Request &r, const Layout &L, char *temp, hipStream_t stream)
+{
+    constexpr int W = sizeof(K) == 8 ? kWaves64 : kWaves32;
+    constexpr int I = sizeof(K) == 8 ? kItems64 : kItems32;
+    if (pairs) return run_passes<K, true, W, I, CODE>(r, L, temp, stream);
+    return run_passes<K, false, W, I, CODE>(r, L, temp, stream);
+}
+
 lrs_status sort_entry(const Request &rq, void *d_temp, size_t *temp_bytes, hipStream_t stream)
 {
     // All checks happen before any HIP call, so they need no device.
     if (temp_bytes == nullptr) return LRS_ERR_INVALID_ARG;
-    const int key_bits = rq.kind == KIND_U64 ? 64 : 32;
+    const int key_bits = 8 * key_bytes(rq.kind);
     const size_t ksz = key_bits / 8;
     if (rq.n < 0 || rq.n > (int64_t)0xFFFFFFFFll) return LRS_ERR_INVALID_ARG;
     if (rq.begin_bit < 0 || rq.end_bit < rq.begin_bit || rq.end_bit > key_bits) return LRS_ERR_INVALID_ARG;
@@ -448,12 +431,15 @@ lrs_status sort_entry(const Request &rq, void *d_temp, size_t *temp_bytes, hipSt
         return st;
     }
     char *temp = (char *)d_temp;
-    if (r.kind == KIND_U64) {
-        if (pairs) return run_passes<uint64_t, true, kWaves64, kItems64>(r, L, temp, stream);
-        return run_passes<uint64_t, false, kWaves64, kItems64>(r, L, temp, stream);
+    switch (r.kind) {
+    case KIND_U32: return run_kind<uint32_t, CODE_UNSIGNED>(pairs, r, L, temp, stream);
+    case KIND_I32: return run_kind<uint32_t, CODE_SIGNED>(pairs, r, L, temp, stream);
+    case KIND_F32: return run_kind<uint32_t, CODE_FLOAT>(pairs, r, L, temp, stream);
+    case KIND_U64: return run_kind<uint64_t, CODE_UNSIGNED>(pairs, r, L, temp, stream);
+    case KIND_I64: return run_kind<uint64_t, CODE_SIGNED>(pairs, r, L, temp, stream);
+    case KIND_F64: return run_kind<uint64_t, CODE_FLOAT>(pairs, r, L, temp, stream);
     }
-    if (pairs) return run_passes<uint32_t, true, kWaves32, kItems32>(r, L, temp, stream);
-    return run_passes<uint32_t, false, kWaves32, kItems32>(r, L, temp, stream);
+    return LRS_ERR_INVALID_ARG;
 }
 
 }  // namespace
@@ -507,6 +493,54 @@ LRS_API lrs_status lrs_sort_pairs_f32(void *d_temp, size_t *temp_bytes, const fl
 {
     if (n > 0 && (!d_values_in || !d_values_out)) return LRS_ERR_INVALID_ARG;
     return sort_entry({KIND_F32, d_keys_in, d_keys_out, d_values_in, d_values_out, n, begin_bit, end_bit}, d_temp,
+                      temp_bytes, stream);
+}
+
+LRS_API lrs_status lrs_sort_keys_i32(void *d_temp, size_t *temp_bytes, const int32_t *d_keys_in, int32_t *d_keys_out,
+                                     int64_t n, int begin_bit, int end_bit, hipStream_t stream)
+{
+    return sort_entry({KIND_I32, d_keys_in, d_keys_out, nullptr, nullptr, n, begin_bit, end_bit}, d_temp,
+                      temp_bytes, stream);
+}
+
+LRS_API lrs_status lrs_sort_keys_i64(void *d_temp, size_t *temp_bytes, const int64_t *d_keys_in, int64_t *d_keys_out,
+                                     int64_t n, int begin_bit, int end_bit, hipStream_t stream)
+{
+    return sort_entry({KIND_I64, d_keys_in, d_keys_out, nullptr, nullptr, n, begin_bit, end_bit}, d_temp,
+                      temp_bytes, stream);
+}
+
+LRS_API lrs_status lrs_sort_keys_f64(void *d_temp, size_t *temp_bytes, const double *d_keys_in, double *d_keys_out,
+                                     int64_t n, int begin_bit, int end_bit, hipStream_t stream)
+{
+    return sort_entry({KIND_F64, d_keys_in, d_keys_out, nullptr, nullptr, n, begin_bit, end_bit}, d_temp,
+                      temp_bytes, stream);
+}
+
+LRS_API lrs_status lrs_sort_pairs_i32(void *d_temp, size_t *temp_bytes, const int32_t *d_keys_in,
+                                      const uint32_t *d_values_in, int32_t *d_keys_out, uint32_t *d_values_out,
+                                      int64_t n, int begin_bit, int end_bit, hipStream_t stream)
+{
+    if (n > 0 && (!d_values_in || !d_values_out)) return LRS_ERR_INVALID_ARG;
+    return sort_entry({KIND_I32, d_keys_in, d_keys_out, d_values_in, d_values_out, n, begin_bit, end_bit}, d_temp,
+                      temp_bytes, stream);
+}
+
+LRS_API lrs_status lrs_sort_pairs_i64(void *d_temp, size_t *temp_bytes, const int64_t *d_keys_in,
+                                      const uint32_t *d_values_in, int64_t *d_keys_out, uint32_t *d_values_out,
+                                      int64_t n, int begin_bit, int end_bit, hipStream_t stream)
+{
+    if (n > 0 && (!d_values_in || !d_values_out)) return LRS_ERR_INVALID_ARG;
+    return sort_entry({KIND_I64, d_keys_in, d_keys_out, d_values_in, d_values_out, n, begin_bit, end_bit}, d_temp,
+                      temp_bytes, stream);
+}
+
+LRS_API lrs_status lrs_sort_pairs_f64(void *d_temp, size_t *temp_bytes, const double *d_keys_in,
+                                      const uint32_t *d_values_in, double *d_keys_out, uint32_t *d_values_out,
+                                      int64_t n, int begin_bit, int end_bit, hipStream_t stream)
+{
+    if (n > 0 && (!d_values_in || !d_values_out)) return LRS_ERR_INVALID_ARG;
+    return sort_entry({KIND_F64, d_keys_in, d_keys_out, d_values_in, d_values_out, n, begin_bit, end_bit}, d_temp,
                       temp_bytes, stream);
 }
 

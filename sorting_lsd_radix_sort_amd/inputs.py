@@ -55,9 +55,19 @@ CONFIGS: dict[str, Config] = {c.name: c for c in [
                        "uint32 index payload"),
     Config("c5b_u32_keys_20bit", "u32", 1 << 26, 5, "uniform20", False, 0, 20,
            description="2^26 uint32 keys uniform on [0, 2^20), seed 5, bits [0,20), keys only"),
+    # other key types through the same kernels (signed integers, float64)
+    Config("f1_i32_keys_1e8", "i32", 100_000_000, 6, "uniform", False, 0, 32,
+           description="1e8 int32 keys, uniform bit patterns (seed 6), keys only, bits [0,32)"),
+    Config("f1_i64_pairs", "i64", 1 << 26, 8, "uniform", True, 0, 64,
+           description="2^26 int64 keys, uniform bit patterns (seed 8), uint32 index payload"),
+    Config("f1_f64_pairs_normal", "f64", 1 << 26, 7, "normal_zeros", True, 0, 64,
+           description="2^26 float64 keys from N(0,1) (seed 7) with ~1% exact +-0.0, "
+                       "uint32 index payload"),
 ]}
 
-KEY_DTYPES = {"u32": np.uint32, "f32": np.float32, "u64": np.uint64}
+KEY_DTYPES = {"u32": np.uint32, "i32": np.int32, "f32": np.float32,
+              "u64": np.uint64, "i64": np.int64, "f64": np.float64}
+_BITS_DTYPE = {4: np.uint32, 8: np.uint64}
 
 
 def draw_keys(cfg: Config, n: int | None = None) -> np.ndarray:
@@ -66,10 +76,9 @@ def draw_keys(cfg: Config, n: int | None = None) -> np.ndarray:
     if cfg.dist == "equal":
         return np.full(n, cfg.const_key, dtype=KEY_DTYPES[cfg.key_type])
     rng = np.random.default_rng(cfg.seed)
-    if cfg.dist == "uniform" and cfg.key_type == "u32":
-        return rng.integers(0, 2**32, size=n, dtype=np.uint32)
-    if cfg.dist == "uniform" and cfg.key_type == "u64":
-        return rng.integers(0, 2**64, size=n, dtype=np.uint64)
+    if cfg.dist == "uniform":
+        dt = np.dtype(KEY_DTYPES[cfg.key_type])
+        return rng.integers(0, 2**(8 * dt.itemsize), size=n, dtype=_BITS_DTYPE[dt.itemsize]).view(dt)
     if cfg.dist == "uniform20":
         return rng.integers(0, 2**20, size=n, dtype=np.uint32)
     if cfg.dist == "and3":
@@ -78,11 +87,12 @@ def draw_keys(cfg: Config, n: int | None = None) -> np.ndarray:
         a &= rng.integers(0, 2**32, size=n, dtype=np.uint32)
         return a
     if cfg.dist == "normal_zeros":
-        x = rng.standard_normal(n).astype(np.float32)
+        dt = KEY_DTYPES[cfg.key_type]
+        x = rng.standard_normal(n).astype(dt)
         zero = rng.random(n) < 0.01
         negative = rng.random(n) < 0.5
-        x[zero & negative] = np.float32(-0.0)
-        x[zero & ~negative] = np.float32(0.0)
+        x[zero & negative] = dt(-0.0)
+        x[zero & ~negative] = dt(0.0)
         assert not np.isnan(x).any()
         return x
     raise ValueError("no generator for %s/%s" % (cfg.dist, cfg.key_type))
@@ -101,36 +111,36 @@ def draw(name: str, n: int | None = None):
 
 
 def random_keys(key_type: str, n: int, seed: int, dist: str = "uniform") -> np.ndarray:
-    """Ad-hoc seeded keys for edge-case tests: "uniform", "dup" (few distinct
-    values, heavy duplicates), "and3" (skewed bits) or "f32mix" (floats with
-    zeros of both signs, infinities and denormals mixed in)."""
+    """Ad-hoc seeded keys for edge-case tests, of any key type: "uniform"
+    (uniform bit patterns), "dup" (few distinct values, heavy duplicates),
+    "and3" (skewed bits: the AND of three uniform words) or "fmix" / "f32mix"
+    (floats from N(0,1) with zeros of both signs, infinities, denormals and the
+    extremes mixed in)."""
     rng = np.random.default_rng(seed)
-    dt = KEY_DTYPES[key_type]
+    dt = np.dtype(KEY_DTYPES[key_type])
+    udt = _BITS_DTYPE[dt.itemsize]
+    bits = 8 * dt.itemsize
     if dist == "uniform":
-        if key_type == "f32":
-            return rng.integers(0, 2**32, size=n, dtype=np.uint32).view(np.float32).copy()
-        return rng.integers(0, 2**(8 * np.dtype(dt).itemsize), size=n, dtype=dt)
+        return rng.integers(0, 2**bits, size=n, dtype=udt).view(dt).copy()
     if dist == "dup":
-        if key_type == "f32":
-            pool = np.concatenate([rng.standard_normal(5).astype(np.float32),
-                                   np.array([0.0, -0.0], dtype=np.float32)])
+        if dt.kind == "f":
+            pool = np.concatenate([rng.standard_normal(5).astype(dt), np.array([0.0, -0.0], dtype=dt)])
         else:
-            pool = rng.integers(0, 2**(8 * np.dtype(dt).itemsize), size=7, dtype=dt)
+            pool = rng.integers(0, 2**bits, size=7, dtype=udt).view(dt)
         return pool[rng.integers(0, len(pool), size=n)]
     if dist == "and3":
-        bits = 8 * np.dtype(dt).itemsize
-        udt = np.uint64 if bits == 64 else np.uint32
         a = rng.integers(0, 2**bits, size=n, dtype=udt)
         a &= rng.integers(0, 2**bits, size=n, dtype=udt)
         a &= rng.integers(0, 2**bits, size=n, dtype=udt)
-        return a.view(np.float32).copy() if key_type == "f32" else a
-    if dist == "f32mix":
-        specials = np.array([0.0, -0.0, np.inf, -np.inf, 1.0, -1.0,
-                             np.finfo(np.float32).tiny, -np.finfo(np.float32).tiny,
-                             np.float32(1e-45), np.float32(-1e-45),
-                             np.finfo(np.float32).max, -np.finfo(np.float32).max],
-                            dtype=np.float32)
-        x = rng.standard_normal(n).astype(np.float32)
+        return a.view(dt).copy()
+    if dist in ("fmix", "f32mix"):
+        if dt.kind != "f":
+            raise ValueError("fmix is for float keys")
+        fi = np.finfo(dt)
+        den = fi.smallest_subnormal
+        specials = np.array([0.0, -0.0, np.inf, -np.inf, 1.0, -1.0, fi.tiny, -fi.tiny,
+                             den, -den, fi.max, -fi.max], dtype=dt)
+        x = rng.standard_normal(n).astype(dt)
         pick = rng.random(n) < 0.3
         x[pick] = specials[rng.integers(0, len(specials), size=int(pick.sum()))]
         return x

@@ -8,9 +8,10 @@ ordered by the key bits [begin_bit, end_bit), it is a permutation of the input
 section 6, fifth pitfall; quant67.com survey, section 11.3, the (value,
 original index) order that makes a sort stable).
 
-For float32 keys the ordering word of a key is the oracle's sign-flip encoding,
-which tests/test_oracle.py pins exhaustively against IEEE-754 ordering; every
-other key type needs no encoding.
+For float and signed keys the ordering word of a key is the oracle's order
+code (float sign-flip, signed sign-bit flip), which tests/test_oracle.py pins
+against IEEE-754 ordering, numpy's signed comparisons and closed forms;
+unsigned keys need no code.
 """
 from __future__ import annotations
 
@@ -18,27 +19,27 @@ import numpy as np
 
 import oracle
 
-UINT_OF = {"u32": np.uint32, "f32": np.uint32, "u64": np.uint64}
+UINT_OF = {"u32": np.uint32, "i32": np.uint32, "f32": np.uint32,
+           "u64": np.uint64, "i64": np.uint64, "f64": np.uint64}
+_TYPE_OF = {np.dtype(np.uint32): "u32", np.dtype(np.int32): "i32", np.dtype(np.float32): "f32",
+            np.dtype(np.uint64): "u64", np.dtype(np.int64): "i64", np.dtype(np.float64): "f64"}
 
 
 def raw_bits(keys: np.ndarray) -> np.ndarray:
-    """Keys as unsigned words of the same width (float32 -> its bit pattern)."""
-    if keys.dtype == np.float32:
-        return keys.view(np.uint32)
-    return keys
+    """Keys as unsigned words of the same width (their bit patterns)."""
+    return keys.view(UINT_OF[_TYPE_OF[keys.dtype]])
 
 
 def key_type_of(keys: np.ndarray) -> str:
-    return {np.dtype(np.uint32): "u32", np.dtype(np.float32): "f32",
-            np.dtype(np.uint64): "u64"}[keys.dtype]
+    return _TYPE_OF[keys.dtype]
 
 
 def order_field(keys: np.ndarray, begin_bit: int, end_bit: int) -> np.ndarray:
     """F(k) = (T(k) >> begin_bit) mod 2^(end_bit - begin_bit) as uint64."""
-    if keys.dtype == np.float32:
-        words = oracle.f2s(keys.view(np.uint32)).astype(np.uint64)
-    else:
+    if keys.dtype in (np.uint32, np.uint64):
         words = keys.astype(np.uint64)
+    else:
+        words = oracle.order_codes(keys)
     width = end_bit - begin_bit
     if width == 0:
         return np.zeros(words.shape, dtype=np.uint64)

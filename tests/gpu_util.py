@@ -7,8 +7,9 @@ import numpy as np
 
 import sorting_lsd_radix_sort_amd as lrs
 
-BITS = {np.dtype(np.uint32): 32, np.dtype(np.float32): 32, np.dtype(np.uint64): 64}
-SFX = {np.dtype(np.uint32): "u32", np.dtype(np.float32): "f32", np.dtype(np.uint64): "u64"}
+SFX = {np.dtype(np.uint32): "u32", np.dtype(np.int32): "i32", np.dtype(np.float32): "f32",
+       np.dtype(np.uint64): "u64", np.dtype(np.int64): "i64", np.dtype(np.float64): "f64"}
+BITS = {dt: 8 * dt.itemsize for dt in SFX}
 
 
 def announce(msg: str) -> None:

@@ -30,7 +30,7 @@ def header_functions():
 def test_library_loads_and_exports_header_symbols():
     lib = lrs.load_library()
     declared = header_functions()
-    assert "lrs_sort_pairs_f32" in declared and len(declared) >= 12
+    assert "lrs_sort_pairs_f64" in declared and len(declared) >= 18
     for name in declared:
         assert hasattr(lib, name), "missing export " + name
     assert set(declared) == set(lrs.EXPORTED)
@@ -50,7 +50,8 @@ def q_pairs(sfx, n, b, e, kin=A, vin=C, kout=B, vout=D):
     return getattr(lrs, "lrs_sort_pairs_" + sfx)(None, 0, kin, vin, kout, vout, n, b, e)
 
 
-@pytest.mark.parametrize("sfx,ksz,bits", [("u32", 4, 32), ("f32", 4, 32), ("u64", 8, 64)])
+@pytest.mark.parametrize("sfx,ksz,bits", [("u32", 4, 32), ("i32", 4, 32), ("f32", 4, 32),
+                                          ("u64", 8, 64), ("i64", 8, 64), ("f64", 8, 64)])
 def test_temp_query_sizes(sfx, ksz, bits):
     n = 100_000_000
     # out-of-place, >= 2 passes: one alternate key buffer plus a small count matrix
@@ -79,7 +80,8 @@ def test_temp_query_small_and_empty():
     assert q_keys("u32", 5, 3, 3) < 64 * 1024     # empty bit range: plain copy
 
 
-@pytest.mark.parametrize("sfx,bits", [("u32", 32), ("f32", 32), ("u64", 64)])
+@pytest.mark.parametrize("sfx,bits", [("u32", 32), ("i32", 32), ("f32", 32), ("u64", 64), ("i64", 64),
+                                      ("f64", 64)])
 def test_invalid_bit_ranges(sfx, bits):
     for b, e in [(-1, 8), (9, 8), (0, bits + 1), (bits + 1, bits + 1)]:
         with pytest.raises(lrs.LrsError) as ei:

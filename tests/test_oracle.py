@@ -201,6 +201,125 @@ def test_f32_partial_range_composes():
         assert np.array_equal(ko.view(np.uint32), oracle.s2f(ku))
 
 
+# ---------------------------------------------------- signed and float64 keys
+
+def _signed_field(bits, b, e):
+    """Order field of a two's-complement value v: its rank among all values of
+    that width is v + 2^(bits-1) (an offset, not the oracle's bit flip)."""
+    mask = (1 << (e - b)) - 1
+    return lambda v: (((v + (1 << (bits - 1))) % (1 << bits)) >> b) & mask
+
+
+def _brute_signed(alphabet, dtype, bits, ranges, max_len):
+    for length in range(0, max_len + 1):
+        for seq in itertools.product(alphabet, repeat=length):
+            keys = np.array(seq, dtype=dtype)
+            pay = np.arange(length, dtype=np.uint32)
+            for b, e in ranges:
+                want = _stable_ref(list(seq), _signed_field(bits, b, e))
+                ko, vo = oracle.sort_pairs(keys, pay, b, e)
+                assert vo.tolist() == want, (seq, b, e)
+                assert ko.tolist() == [seq[i] for i in want]
+
+
+def test_bruteforce_i32():
+    _brute_signed([-2**31, -1, 0, 2**31 - 1], np.int32, 32, RANGES_U32, 5)
+    _brute_signed([-256, 255, 1, -2], np.int32, 32, RANGES_U32, 5)
+
+
+def test_bruteforce_i64():
+    ranges = [(0, 64), (0, 40), (32, 64), (5, 61), (63, 64), (56, 64)]
+    _brute_signed([-2**63, -1, 0, 2**63 - 1], np.int64, 64, ranges, 5)
+    _brute_signed([-(1 << 40), (1 << 40) - 1, 7, -8], np.int64, 64, ranges, 4)
+
+
+@pytest.mark.parametrize("key_type", ["i32", "i64"])
+@pytest.mark.parametrize("dist", ["uniform", "dup", "and3"])
+def test_numpy_stable_argsort_signed(key_type, dist):
+    """Full-range signed sorts equal numpy's stable argsort of the values."""
+    keys = inputs.random_keys(key_type, 200_003, 9, dist)
+    ko, vo = oracle.sort_pairs(keys, np.arange(keys.size, dtype=np.uint32))
+    want = np.argsort(keys, kind="stable")
+    assert np.array_equal(vo, want.astype(np.uint32))
+    assert np.array_equal(ko, keys[want])
+    assert np.array_equal(oracle.sort_keys(keys), np.sort(keys))
+
+
+def test_bruteforce_f64_full_range():
+    """Full-range float64 sort equals Python's stable sort by (value, sign of zero)."""
+    alpha = [-0.0, 0.0, math.inf, -1.0, 5e-324]
+    for length in range(0, 6):
+        for seq in itertools.product(alpha, repeat=length):
+            keys = np.array(seq, dtype=np.float64)
+            want = _stable_ref(keys.tolist(), lambda x: (x, math.copysign(1.0, x)))
+            ko, vo = oracle.sort_pairs(keys, np.arange(length, dtype=np.uint32))
+            assert vo.tolist() == want, seq
+            assert ko.view(np.uint64).tolist() == keys.view(np.uint64)[want].tolist()
+
+
+def test_numpy_lexsort_f64():
+    """Full-range float64 pair sort equals numpy's stable lexsort by
+    (value, then -0.0 before +0.0)."""
+    x = inputs.random_keys("f64", 300_001, 6, "fmix")
+    ko, vo = oracle.sort_pairs(x, np.arange(x.size, dtype=np.uint32))
+    want = np.lexsort((~np.signbit(x), x))
+    assert np.array_equal(vo, want.astype(np.uint32))
+    assert np.array_equal(ko.view(np.uint64), x.view(np.uint64)[want])
+
+
+def test_f64_code_order_and_round_trip():
+    """On random non-NaN doubles of every scale, the float64 code orders as the
+    FPU compares (with -0.0 below +0.0); on random bit patterns, NaNs included,
+    the inverse restores every pattern."""
+    rng = np.random.default_rng(17)
+    pats = rng.integers(0, 2**64, size=4000, dtype=np.uint64)
+    for p in pats.tolist():
+        assert oracle.f64_uncode(oracle.order_code(p, oracle.KIND_F64)) == p
+    vals = pats.view(np.float64)
+    vals = vals[~np.isnan(vals)]
+    specials = np.array([0.0, -0.0, np.inf, -np.inf, 5e-324, -5e-324, 2.2250738585072014e-308,
+                         -1.7976931348623157e308, 1.0, -1.0], dtype=np.float64)
+    vals = np.concatenate([vals, specials])
+    codes = oracle.order_codes(vals)
+    a, b = rng.integers(0, vals.size, size=(2, 20000))
+    for i, j in zip(a.tolist(), b.tolist()):
+        x, y = float(vals[i]), float(vals[j])
+        kx, ky = (x, math.copysign(1.0, x)), (y, math.copysign(1.0, y))
+        assert (kx < ky) == (int(codes[i]) < int(codes[j])), (x, y)
+
+
+def test_f64_nan_reading():
+    """As for float32: positive NaNs after +inf, negative NaNs before -inf."""
+    pats = np.array([0x7FF8000000000000, 0x7FF0000000000000, 0xFFF8000000000000,
+                     0xFFF0000000000000, 0x0, 0x7FF0000000000001, 0xFFFFFFFFFFFFFFFF],
+                    dtype=np.uint64)
+    out = oracle.sort_keys(pats.view(np.float64)).view(np.uint64)
+    assert out.tolist() == [0xFFFFFFFFFFFFFFFF, 0xFFF8000000000000, 0xFFF0000000000000, 0x0,
+                            0x7FF0000000000000, 0x7FF0000000000001, 0x7FF8000000000000]
+
+
+@pytest.mark.parametrize("key_type", ["i32", "i64", "f64"])
+def test_partial_range_composes(key_type):
+    """A sort over [b,e) of signed or float64 keys is the unsigned sort of their
+    order words over [b,e), mapped back: both pieces are pinned above."""
+    dist = "fmix" if key_type == "f64" else "dup"
+    x = inputs.random_keys(key_type, 4000, 21, dist)
+    bits = 8 * x.dtype.itemsize
+    rng = np.random.default_rng(3)
+    words = oracle.order_codes(x)
+    if bits == 32:
+        words = words.astype(np.uint32)
+    for b, e in [(0, 20), (8, 16), (3, 17), (bits - 1, bits), (bits - 16, bits)]:
+        pay = rng.permutation(x.size).astype(np.uint32)
+        ko, vo = oracle.sort_pairs(x, pay, b, e)
+        ku, vu = oracle.sort_pairs(words, pay, b, e)
+        assert np.array_equal(vo, vu)
+        kind = {"i32": oracle.KIND_I32, "i64": oracle.KIND_I64, "f64": oracle.KIND_F64}[key_type]
+        back = [oracle.f64_uncode(int(w)) if key_type == "f64" else oracle.order_code(int(w), kind)
+                for w in ku.tolist()]
+        assert ko.view(words.dtype).tolist() == back
+
+
 # ------------------------------------------------------- library cross-check
 
 @pytest.mark.parametrize("key_type,dist", [("u32", "uniform"), ("u32", "dup"), ("u32", "and3"),

@@ -28,8 +28,12 @@ TILE = 8192  # keys per downsweep tile
 SMALL_SIZES = [0, 1, 2, 3, 63, 64, 65, 255, 256, 257, 1023, 1024, 1025, 4095, 4096, 4097,
                TILE - 1, TILE, TILE + 1, 2 * TILE, 3 * TILE + 17, 65_536]
 RANGES = {"u32": [(0, 32), (0, 20), (8, 16), (3, 17), (31, 32), (24, 32), (5, 5)],
+          "i32": [(0, 32), (0, 20), (16, 32), (31, 32), (28, 32)],
           "f32": [(0, 32), (0, 20), (16, 32), (31, 32)],
-          "u64": [(0, 64), (0, 40), (32, 64), (5, 61), (63, 64)]}
+          "u64": [(0, 64), (0, 40), (32, 64), (5, 61), (63, 64)],
+          "i64": [(0, 64), (32, 64), (5, 61), (63, 64)],
+          "f64": [(0, 64), (0, 40), (48, 64), (63, 64)]}
+KEY_TYPES = ["u32", "i32", "f32", "u64", "i64", "f64"]
 
 
 def _compare(keys, vals, b, e, **kw):
@@ -48,7 +52,7 @@ def _compare(keys, vals, b, e, **kw):
 
 # ------------------------------------------------------------ small sizes, oracle
 
-@pytest.mark.parametrize("key_type", ["u32", "f32", "u64"])
+@pytest.mark.parametrize("key_type", KEY_TYPES)
 @pytest.mark.parametrize("pairs", [False, True])
 def test_small_sizes_all_ranges(key_type, pairs):
     for n in SMALL_SIZES:
@@ -61,7 +65,9 @@ def test_small_sizes_all_ranges(key_type, pairs):
 
 
 @pytest.mark.parametrize("key_type,dist", [("u32", "and3"), ("u64", "and3"), ("f32", "f32mix"),
-                                           ("u32", "dup"), ("f32", "uniform")])
+                                           ("u32", "dup"), ("f32", "uniform"), ("i32", "and3"),
+                                           ("i32", "uniform"), ("i64", "dup"), ("i64", "uniform"),
+                                           ("f64", "fmix"), ("f64", "uniform")])
 def test_skewed_and_special_values(key_type, dist):
     n = 5 * TILE + 1234
     keys = inputs.random_keys(key_type, n, 77, dist)
@@ -78,7 +84,8 @@ REDUCED = {"c1_u32_keys_64k": None, "c2_u32_keys_1e8": 4_194_304 + 1237,
            "c3a_u32_pairs_and3": 2_097_152 + 999, "c3b_u32_pairs_equal": 2_097_152 + 5,
            "c3b0_u32_pairs_zero": 1_000_003, "c4_f32_pairs_normal": 2_097_152 + 77,
            "c5a_u64_pairs": 1_048_576 + 4095, "c5b_u32_pairs_20bit": 2_097_152 + 1,
-           "c5b_u32_keys_20bit": 2_097_152 + 4097}
+           "c5b_u32_keys_20bit": 2_097_152 + 4097, "f1_i32_keys_1e8": 3_000_017,
+           "f1_i64_pairs": 1_048_576 + 3, "f1_f64_pairs_normal": 1_048_576 + 8191}
 
 
 @pytest.mark.parametrize("name", list(REDUCED))
@@ -89,24 +96,25 @@ def test_workloads_reduced_vs_oracle(name):
 
 
 @pytest.mark.parametrize("key_type,n,pairs", [("u32", 12_500_003, False), ("f32", 9_000_001, True),
-                                              ("u64", 6_000_011, True)])
+                                              ("u64", 6_000_011, True), ("i32", 7_000_003, True),
+                                              ("i64", 5_000_017, False), ("f64", 5_000_011, True)])
 def test_multi_tile_blocks_vs_oracle(key_type, n, pairs):
     """Large enough that each workgroup walks several tiles of its block."""
-    keys = inputs.random_keys(key_type, n, 31, "uniform" if key_type != "f32" else "f32mix")
+    keys = inputs.random_keys(key_type, n, 31, "fmix" if key_type in ("f32", "f64") else "uniform")
     vals = np.arange(n, dtype=np.uint32) if pairs else None
-    bits = 64 if key_type == "u64" else 32
+    bits = 8 * keys.dtype.itemsize
     announce("multi-tile %s n=%d pairs=%s" % (key_type, n, pairs))
     _compare(keys, vals, 0, bits)
 
 
 # ------------------------------------------------------------------ in-place use
 
-@pytest.mark.parametrize("key_type", ["u32", "f32", "u64"])
+@pytest.mark.parametrize("key_type", KEY_TYPES)
 def test_in_place(key_type):
     n = 3 * TILE + 101
-    keys = inputs.random_keys(key_type, n, 9, "dup" if key_type != "f32" else "f32mix")
+    keys = inputs.random_keys(key_type, n, 9, "fmix" if key_type in ("f32", "f64") else "dup")
     vals = np.random.default_rng(3).permutation(n).astype(np.uint32)
-    bits = 64 if key_type == "u64" else 32
+    bits = 8 * keys.dtype.itemsize
     # 1, 2, 3 and 4 passes (odd pass counts need the second alternate buffer)
     for b, e in [(0, 8), (0, 16), (0, 24), (bits - 32, bits), (4, 9)]:
         for ipk, ipv in [(True, False), (False, True), (True, True)]:
@@ -191,7 +199,7 @@ def test_profiling_records_every_launch():
 
 FULL = ["c1_u32_keys_64k", "c2_u32_keys_1e8", "c3a_u32_pairs_and3", "c3b_u32_pairs_equal",
         "c3b0_u32_pairs_zero", "c4_f32_pairs_normal", "c5a_u64_pairs", "c5b_u32_pairs_20bit",
-        "c5b_u32_keys_20bit"]
+        "c5b_u32_keys_20bit", "f1_i32_keys_1e8", "f1_i64_pairs", "f1_f64_pairs_normal"]
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -205,6 +213,7 @@ def test_workloads_full_size(name):
             assert np.array_equal(got_v, vals) and np.array_equal(got_k, keys)
     else:
         # every key bit lies in the sorted range, so the output is numpy's sort
+        # (numpy orders signed integers by value, as their order code does)
         assert int(checks.raw_bits(keys).max()) < (1 << cfg.end_bit) and cfg.begin_bit == 0
         i = checks.first_mismatch(got_k, np.sort(keys))
         assert i < 0, "mismatch with np.sort at %d" % i
