@@ -168,7 +168,7 @@ def main() -> int:
 
     # ---- per-kernel durations: same K steps again with events around each launch
     log("[bench] per-kernel events over %d steps" % args.steps)
-    lrs.lrs_prof_start(args.steps * 3 * passes + 16)
+    lrs.lrs_prof_start(args.steps * (3 * passes + 1) + 16)  # + the finalize launch of each sort
     try:
         for _ in range(args.steps):
             step()

@@ -180,18 +180,54 @@ __device__ __forceinline__ uint4 wave_scan_digits(uint4 c)
     return make_uint4(base, base + p1, base + p2, base + p3);
 }
 
+// ------------------------------------------------------------------ routing
+//
+// Where a sort's data can be: the caller's input and output and two alternate
+// buffers in temp storage, by index.  A pass whose digit is the same for every
+// key leaves the order unchanged, so it moves nothing (the kwkr.cn essay on
+// bitonic vs. LSD radix sort, section 3.4: a pass over a constant digit is
+// wasted work).  Which buffer holds the data is then known only on the device:
+// the downsweep of pass p records it in route[p + 1], separately for keys and
+// values, and the kernels of the next pass read it there.
+enum BufIndex { BUF_IN = 0, BUF_OUT = 1, BUF_A = 2, BUF_B = 3 };
+
+struct SortBufs {
+    const void *keys[4];
+    const uint32_t *vals[4];
+};
+
+// The buffer a pass reads: fixed for the first pass, recorded for the others.
+__device__ __forceinline__ int pass_source(const uint32_t *route, int pass, int fixed)
+{
+    return fixed >= 0 ? fixed : (int)route[pass];
+}
+
+// Where a pass leaves its data.  A skipped pass leaves it in place.  A pass
+// that runs writes its planned buffer, or, when the data already sits there
+// (earlier skips changed the parity), the other alternate; the last pass
+// writes the output whenever the data is not already in it.  Data left outside
+// the output at the end is moved by the finalize kernel.
+__device__ __forceinline__ int pass_dest(int src, int planned, bool last, bool skip)
+{
+    if (skip) return src;
+    if (last) return src != BUF_OUT ? BUF_OUT : BUF_A;
+    if (planned != src) return planned;
+    return src == BUF_A ? BUF_OUT : BUF_A;
+}
+
 // -------------------------------------------------------------------- upsweep
 
 // Counts the digits of block b = keys [b * block_len, min(n, (b+1) * block_len)).
 // Each wave adds into its own LDS sub-histograms, so atomics only contend
 // within a wave (the kwkr.cn essay, section 3.2, and the quant67.com survey,
 // section 8.1: per-block and per-warp counting instead of global atomics).
-// VEC loads 16 bytes per lane when the key array is 16-byte aligned.
-template <typename K, int CODE, int THREADS, bool VEC>
+// The keys are read 16 bytes per lane when their array is 16-byte aligned.
+template <typename K, int CODE, int THREADS>
 __global__ __launch_bounds__(THREADS) void upsweep_kernel(
-    const K *__restrict__ keys, uint32_t *__restrict__ counts, int64_t n, int64_t block_len,
-    int num_blocks, int shift, uint32_t mask)
+    SortBufs bufs, const uint32_t *__restrict__ route, int pass, int src_fixed, uint32_t *__restrict__ counts,
+    int64_t n, int64_t block_len, int num_blocks, int shift, uint32_t mask)
 {
+    const K *__restrict__ keys = (const K *)bufs.keys[pass_source(route, pass, src_fixed)];
     constexpr int WAVES = THREADS / kWave;
     // COPIES sub-histograms per wave (lane % COPIES picks one), padded by one
     // word so that equal digits in different copies fall in different banks:
@@ -212,7 +248,7 @@ __global__ __launch_bounds__(THREADS) void upsweep_kernel(
     };
 
     int64_t scalar_from = begin;
-    if constexpr (VEC) {
+    if (((uintptr_t)keys & 15) == 0) {
         // 16-byte vectors: 4 uint32 or 2 uint64 keys each.  `begin` is a whole
         // number of tiles, hence of vectors.
         constexpr int PER = 16 / (int)sizeof(K);
@@ -383,8 +419,8 @@ __device__ __forceinline__ void finish_tile(K (&k)[ITEMS], int first, int valid,
 // tile.
 template <typename K, bool PAIRS, int WAVES, int ITEMS, int SUB, int CODE>
 __global__ __launch_bounds__(WAVES * kWave) void downsweep_kernel(
-    const K *__restrict__ keys_in, K *__restrict__ keys_out, const uint32_t *__restrict__ vals_in,
-    uint32_t *__restrict__ vals_out, const uint32_t *__restrict__ counts,
+    SortBufs bufs, uint32_t *__restrict__ route_k, uint32_t *__restrict__ route_v, int pass, int ksrc_fixed,
+    int vsrc_fixed, int kplanned, int vplanned, int last, const uint32_t *__restrict__ counts,
     const uint32_t *__restrict__ row_total, int64_t n, int64_t block_len, int count_cols, int split, int shift,
     uint32_t mask)
 {
@@ -404,6 +440,28 @@ __global__ __launch_bounds__(WAVES * kWave) void downsweep_kernel(
     const int64_t blk_begin = (int64_t)blk * block_len;
     const int64_t blk_end = blk_begin + block_len < n ? blk_begin + block_len : n;
     const uint32_t n32 = (uint32_t)n;
+
+    // Routing of this pass, and whether it is skipped: it is when one digit
+    // holds every key (each wave tests the 256 totals itself, so the decision
+    // is uniform without a barrier).
+    const int ksrc = pass_source(route_k, pass, ksrc_fixed);
+    const int vsrc = PAIRS ? pass_source(route_v, pass, vsrc_fixed) : 0;
+    bool skip;
+    {
+        const uint4 t = reinterpret_cast<const uint4 *>(row_total)[lane];
+        skip = __ballot(t.x == n32 || t.y == n32 || t.z == n32 || t.w == n32) != 0;
+    }
+    const int kdst = pass_dest(ksrc, kplanned, last != 0, skip);
+    const int vdst = PAIRS ? pass_dest(vsrc, vplanned, last != 0, skip) : 0;
+    if (blk == 0 && tid == 0) {
+        route_k[pass + 1] = (uint32_t)kdst;
+        if constexpr (PAIRS) route_v[pass + 1] = (uint32_t)vdst;
+    }
+    const K *__restrict__ keys_in = (const K *)bufs.keys[ksrc];
+    K *__restrict__ keys_out = (K *)bufs.keys[kdst];
+    const uint32_t *__restrict__ vals_in = PAIRS ? bufs.vals[vsrc] : nullptr;
+    uint32_t *__restrict__ vals_out = PAIRS ? (uint32_t *)bufs.vals[vdst] : nullptr;
+    if (skip) return;  // nothing to reorder
 
     if (wave == 0) {
         // digit starts (exclusive prefix of the row totals), plus this block's
@@ -631,6 +689,40 @@ __global__ __launch_bounds__(WAVES * kWave) void downsweep_kernel(
         if constexpr (SUB == 2) store_full(0);
         store_last(SUB - 1, (int)(blk_end - ta - TILE));
     }
+}
+
+// ------------------------------------------------------------------- finalize
+
+// Grid-stride copy of n elements, 16 bytes per lane per step when both arrays
+// are 16-byte aligned.
+template <typename T>
+__device__ __forceinline__ void grid_copy(const T *__restrict__ src, T *__restrict__ dst, int64_t n)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t first = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    int64_t done = 0;
+    if ((((uintptr_t)src | (uintptr_t)dst) & 15) == 0) {
+        constexpr int PER = 16 / (int)sizeof(T);
+        const int64_t nv = n / PER;
+        const u32x4 *s4 = reinterpret_cast<const u32x4 *>(src);
+        u32x4 *d4 = reinterpret_cast<u32x4 *>(dst);
+        for (int64_t i = first; i < nv; i += stride) d4[i] = __builtin_nontemporal_load(&s4[i]);
+        done = nv * PER;
+    }
+    for (int64_t i = done + first; i < n; i += stride) dst[i] = src[i];
+}
+
+// After the last pass: if the keys (or values) ended outside the output --
+// after skipped passes, or a one-pass in-place sort -- copies them there.
+// Otherwise every workgroup returns at once.
+template <typename K, bool PAIRS>
+__global__ __launch_bounds__(256) void finalize_kernel(SortBufs bufs, const uint32_t *__restrict__ route_k,
+                                                       const uint32_t *__restrict__ route_v, int slot, int64_t n)
+{
+    const int k = (int)route_k[slot];
+    const int v = PAIRS ? (int)route_v[slot] : BUF_OUT;
+    if (k != BUF_OUT) grid_copy<K>((const K *)bufs.keys[k], (K *)bufs.keys[BUF_OUT], n);
+    if (PAIRS && v != BUF_OUT) grid_copy<uint32_t>(bufs.vals[v], (uint32_t *)bufs.vals[BUF_OUT], n);
 }
 
 // ----------------------------------------------------------------------- copy

@@ -42,6 +42,7 @@ int key_code(KeyKind k)
 
 constexpr int kMaxBlocks = 4096;  // count-matrix width cap (scan: 256 threads x 16)
 constexpr int kMaxSplit = 8;      // upsweep sub-blocks per downsweep block
+constexpr int kMaxRoute = 16;     // route entries per array: passes + 1 (at most 9)
 constexpr int kUpsweepThreads = 512;
 constexpr int kScanThreads = 256;
 constexpr int kScanPerThread = kMaxBlocks / kScanThreads;
@@ -142,7 +143,6 @@ struct Plan {
     int dst[64];
     bool need_a = false;
     bool need_b = false;
-    bool copy_a_to_out = false;
 };
 
 Plan make_plan(int passes, bool in_place)
@@ -157,8 +157,7 @@ Plan make_plan(int passes, bool in_place)
     }
     pl.need_a = true;
     if (passes == 1) {
-        pl.dst[0] = BUF_A;
-        pl.copy_a_to_out = true;
+        pl.dst[0] = BUF_A;  // the finalize kernel copies it back
         return pl;
     }
     pl.need_b = true;
@@ -191,7 +190,7 @@ struct Layout {
     int64_t tiles = 0;
     int max_cols = 0;  // count-matrix columns (upsweep sub-blocks) at most
     Plan kplan, vplan;
-    size_t off_counts = 0, off_rowtot = 0, off_ka = 0, off_kb = 0, off_va = 0, off_vb = 0;
+    size_t off_counts = 0, off_rowtot = 0, off_route = 0, off_ka = 0, off_kb = 0, off_va = 0, off_vb = 0;
     size_t total = 0;
 };
 
@@ -210,6 +209,8 @@ Layout make_layout(const Request &rq)
     off += align_up((size_t)kRadix * L.max_cols * 4);
     L.off_rowtot = off;
     off += align_up((size_t)kRadix * 4);
+    L.off_route = off;  // where keys, then values, are before each pass and at the end
+    off += align_up((size_t)2 * kMaxRoute * 4);
     const size_t kbytes = align_up((size_t)rq.n * ksz), vbytes = align_up((size_t)rq.n * 4);
     if (L.kplan.need_a) { L.off_ka = off; off += kbytes; }
     if (L.kplan.need_b) { L.off_kb = off; off += kbytes; }
@@ -255,17 +256,12 @@ lrs_status copy_bytes(void *dst, const void *src, size_t bytes, hipStream_t stre
 // ------------------------------------------------------------ pass launchers
 
 template <typename K, int CODE>
-hipError_t launch_upsweep(const K *keys, uint32_t *counts, int64_t n, int64_t block_len, int blocks, int shift,
-                          uint32_t mask, hipStream_t stream)
+hipError_t launch_upsweep(const SortBufs &bufs, const uint32_t *route, int pass, int src_fixed, uint32_t *counts,
+                          int64_t n, int64_t block_len, int blocks, int shift, uint32_t mask, hipStream_t stream)
 {
-    const bool vec = ((uintptr_t)keys % 16) == 0;
     return launch(LRS_KERNEL_UPSWEEP, stream, [&] {
-        if (vec)
-            upsweep_kernel<K, CODE, kUpsweepThreads, true>
-                <<<blocks, kUpsweepThreads, 0, stream>>>(keys, counts, n, block_len, blocks, shift, mask);
-        else
-            upsweep_kernel<K, CODE, kUpsweepThreads, false>
-                <<<blocks, kUpsweepThreads, 0, stream>>>(keys, counts, n, block_len, blocks, shift, mask);
+        upsweep_kernel<K, CODE, kUpsweepThreads><<<blocks, kUpsweepThreads, 0, stream>>>(
+            bufs, route, pass, src_fixed, counts, n, block_len, blocks, shift, mask);
     });
 }
 
@@ -295,14 +291,22 @@ auto downsweep_fn()
     return downsweep_kernel<K, PAIRS, WAVES, ITEMS, sub_tiles<K, PAIRS>(), CODE>;
 }
 
+struct PassRoute {
+    int pass;
+    int ksrc_fixed, vsrc_fixed;  // first pass: where the data is; later passes: -1
+    int kplanned, vplanned;      // planned destinations
+    int last;
+};
+
 template <typename K, bool PAIRS, int WAVES, int ITEMS, int CODE>
-hipError_t launch_downsweep(const K *kin, K *kout, const uint32_t *vin, uint32_t *vout, const uint32_t *counts,
-                            const uint32_t *rowtot, int64_t n, int64_t block_len, int blocks, int cols, int split,
-                            int shift, uint32_t mask, hipStream_t stream)
+hipError_t launch_downsweep(const SortBufs &bufs, uint32_t *route_k, uint32_t *route_v, const PassRoute &pr,
+                            const uint32_t *counts, const uint32_t *rowtot, int64_t n, int64_t block_len,
+                            int blocks, int cols, int split, int shift, uint32_t mask, hipStream_t stream)
 {
     return launch(LRS_KERNEL_DOWNSWEEP, stream, [&] {
         downsweep_fn<K, PAIRS, WAVES, ITEMS, CODE>()<<<blocks, WAVES * 64, 0, stream>>>(
-            kin, kout, vin, vout, counts, rowtot, n, block_len, cols, split, shift, mask);
+            bufs, route_k, route_v, pr.pass, pr.ksrc_fixed, pr.vsrc_fixed, pr.kplanned, pr.vplanned, pr.last,
+            counts, rowtot, n, block_len, cols, split, shift, mask);
     });
 }
 
@@ -339,7 +343,7 @@ lrs_status run_passes(const Request &rq, const Layout &L, char *temp, hipStream_
     // occupancy allows; the count matrix has one column per sub-block.
     int cus = 0, up_per_cu = 0;
     if (device_cus(&cus) != hipSuccess) return LRS_ERR_HIP;
-    if (occupancy((const void *)upsweep_kernel<K, CODE, kUpsweepThreads, true>, kUpsweepThreads, &up_per_cu) !=
+    if (occupancy((const void *)upsweep_kernel<K, CODE, kUpsweepThreads>, kUpsweepThreads, &up_per_cu) !=
         hipSuccess)
         return LRS_ERR_HIP;
     int split = 1;
@@ -351,41 +355,48 @@ lrs_status run_passes(const Request &rq, const Layout &L, char *temp, hipStream_
 
     uint32_t *counts = (uint32_t *)(temp + L.off_counts);
     uint32_t *rowtot = (uint32_t *)(temp + L.off_rowtot);
-    const K *kbuf_const[4] = {(const K *)rq.keys_in, (const K *)rq.keys_out, (const K *)(temp + L.off_ka),
-                              (const K *)(temp + L.off_kb)};
-    K *kbuf[4] = {nullptr, (K *)rq.keys_out, (K *)(temp + L.off_ka), (K *)(temp + L.off_kb)};
-    const uint32_t *vbuf_const[4] = {rq.vals_in, rq.vals_out, (const uint32_t *)(temp + L.off_va),
-                                     (const uint32_t *)(temp + L.off_vb)};
-    uint32_t *vbuf[4] = {nullptr, rq.vals_out, (uint32_t *)(temp + L.off_va), (uint32_t *)(temp + L.off_vb)};
+    uint32_t *route_k = (uint32_t *)(temp + L.off_route);
+    uint32_t *route_v = route_k + kMaxRoute;
+    SortBufs bufs;
+    bufs.keys[BUF_IN] = rq.keys_in;
+    bufs.keys[BUF_OUT] = rq.keys_out;
+    bufs.keys[BUF_A] = L.kplan.need_a ? temp + L.off_ka : nullptr;
+    bufs.keys[BUF_B] = L.kplan.need_b ? temp + L.off_kb : nullptr;
+    bufs.vals[BUF_IN] = rq.vals_in;
+    bufs.vals[BUF_OUT] = rq.vals_out;
+    bufs.vals[BUF_A] = PAIRS && L.vplan.need_a ? (const uint32_t *)(temp + L.off_va) : nullptr;
+    bufs.vals[BUF_B] = PAIRS && L.vplan.need_b ? (const uint32_t *)(temp + L.off_vb) : nullptr;
+    // An in-place array starts in the output buffer (the same memory).
+    const int kstart = rq.keys_in == rq.keys_out ? BUF_OUT : BUF_IN;
+    const int vstart = PAIRS && rq.vals_in == rq.vals_out ? BUF_OUT : BUF_IN;
 
-    int ksrc = BUF_IN, vsrc = BUF_IN;
     for (int p = 0; p < L.passes; ++p) {
         const int shift = rq.begin_bit + kRadixBits * p;
         const int width = std::min(kRadixBits, rq.end_bit - shift);
         const uint32_t mask = (1u << width) - 1u;
-        const int kdst = L.kplan.dst[p], vdst = L.vplan.dst[p];
+        PassRoute pr;
+        pr.pass = p;
+        pr.ksrc_fixed = p == 0 ? kstart : -1;
+        pr.vsrc_fixed = p == 0 ? vstart : -1;
+        pr.kplanned = L.kplan.dst[p];
+        pr.vplanned = L.vplan.dst[p];
+        pr.last = p == L.passes - 1;
 
-        hipError_t err = launch_upsweep<K, CODE>(kbuf_const[ksrc], counts, rq.n, sub_len, cols, shift, mask, stream);
+        hipError_t err = launch_upsweep<K, CODE>(bufs, route_k, p, pr.ksrc_fixed, counts, rq.n, sub_len, cols, shift,
+                                                 mask, stream);
         if (err != hipSuccess) return LRS_ERR_HIP;
         if (launch_scan(counts, rowtot, cols, stream) != hipSuccess) return LRS_ERR_HIP;
-        err = launch_downsweep<K, PAIRS, WAVES, ITEMS, CODE>(kbuf_const[ksrc], kbuf[kdst],
-                                                             PAIRS ? vbuf_const[vsrc] : nullptr,
-                                                             PAIRS ? vbuf[vdst] : nullptr, counts, rowtot, rq.n,
+        err = launch_downsweep<K, PAIRS, WAVES, ITEMS, CODE>(bufs, route_k, route_v, pr, counts, rowtot, rq.n,
                                                              block_len, blocks, cols, split, shift, mask, stream);
         if (err != hipSuccess) return LRS_ERR_HIP;
-        ksrc = kdst;
-        vsrc = vdst;
     }
-    const size_t ksz = sizeof(K);
-    if (L.kplan.copy_a_to_out) {
-        lrs_status st = copy_bytes(rq.keys_out, temp + L.off_ka, (size_t)rq.n * ksz, stream);
-        if (st != LRS_OK) return st;
-    }
-    if (PAIRS && L.vplan.copy_a_to_out) {
-        lrs_status st = copy_bytes(rq.vals_out, temp + L.off_va, (size_t)rq.n * 4, stream);
-        if (st != LRS_OK) return st;
-    }
-    return LRS_OK;
+    // The data is in the output unless skipped passes left it elsewhere (or a
+    // one-pass in-place sort went through an alternate buffer).
+    const int fin_grid = (int)std::min<int64_t>(((int64_t)sizeof(K) * rq.n + 4095) / 4096, 4096);
+    const hipError_t err = launch(LRS_KERNEL_FINALIZE, stream, [&] {
+        finalize_kernel<K, PAIRS><<<fin_grid, 256, 0, stream>>>(bufs, route_k, route_v, L.passes, rq.n);
+    });
+    return err == hipSuccess ? LRS_OK : LRS_ERR_HIP;
 }
 
 template <typename K, int CODE>

@@ -185,13 +185,13 @@ def test_profiling_records_every_launch():
     announce("profiling hooks")
     lrs.lrs_prof_start(64)
     try:
-        lrs.sort_keys(keys)           # 8 passes x 3 kernels
+        lrs.sort_keys(keys)           # 8 passes x 3 kernels, then the finalize check
         torch.cuda.synchronize()
         lrs.lrs_prof_stop()
         recs = [lrs.lrs_prof_read(i) for i in range(lrs.lrs_prof_count())]
     finally:
         lrs.lrs_prof_release()
-    assert [k for k, _ in recs] == [0, 1, 2] * 8
+    assert [k for k, _ in recs] == [0, 1, 2] * 8 + [4]
     assert all(ms > 0 for _, ms in recs)
 
 
@@ -217,3 +217,47 @@ def test_workloads_full_size(name):
         assert int(checks.raw_bits(keys).max()) < (1 << cfg.end_bit) and cfg.begin_bit == 0
         i = checks.first_mismatch(got_k, np.sort(keys))
         assert i < 0, "mismatch with np.sort at %d" % i
+
+
+# ------------------------------------------------- passes over a constant digit
+
+def _with_constant_digits(keys, digits, bits):
+    """Keys whose listed 8-bit digits are set to a fixed value (the others random)."""
+    udt = np.uint64 if bits == 64 else np.uint32
+    k = keys.view(udt).copy()
+    for d in digits:
+        m = udt(0xFF) << udt(8 * d)
+        k = (k & ~m) | (udt(0xA5 ^ d) << udt(8 * d))
+    return k.view(keys.dtype)
+
+
+@pytest.mark.parametrize("digits", [(0,), (1,), (3,), (0, 1), (1, 2), (0, 1, 2), (0, 1, 2, 3), (1, 3), (2,)])
+@pytest.mark.parametrize("pairs", [False, True])
+def test_constant_digit_passes_vs_oracle(digits, pairs):
+    """A pass whose digit is the same for every key moves nothing; the data then
+    sits elsewhere than planned, later passes and the final copy follow it.
+    Covers skipped first, middle and last passes, odd and even numbers of skips
+    before a pass that runs, and all passes skipped."""
+    n = 5 * TILE + 777
+    base = inputs.random_keys("u32", n, 123, "uniform")
+    keys = _with_constant_digits(base, digits, 32)
+    vals = np.random.default_rng(4).permutation(n).astype(np.uint32) if pairs else None
+    for b, e in [(0, 32), (8, 32), (0, 24), (0, 16)]:
+        announce("constant digits %s pairs=%s bits=[%d,%d)" % (digits, pairs, b, e))
+        _compare(keys, vals, b, e)
+        for ipk, ipv in ([(True, False), (False, True), (True, True)] if pairs else [(True, False)]):
+            announce("constant digits %s in-place keys=%s vals=%s bits=[%d,%d)" % (digits, ipk, ipv, b, e))
+            _compare(keys, vals, b, e, in_place_keys=ipk, in_place_vals=ipv)
+
+
+@pytest.mark.parametrize("key_type", ["u64", "f32", "i64"])
+def test_constant_digit_passes_other_types(key_type):
+    n = 3 * TILE + 55
+    base = inputs.random_keys(key_type, n, 7, "uniform")
+    bits = 8 * base.dtype.itemsize
+    for digits in [(1,), (bits // 8 - 1,), (0, 2, 4), tuple(range(bits // 8))]:
+        keys = _with_constant_digits(base, [d for d in digits if d < bits // 8], bits)
+        vals = np.arange(n, dtype=np.uint32)
+        announce("constant digits %s %s" % (digits, key_type))
+        _compare(keys, vals, 0, bits)
+        _compare(keys, vals, 0, bits, in_place_keys=True, in_place_vals=True)
