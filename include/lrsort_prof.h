@@ -23,8 +23,9 @@ typedef enum lrs_kernel_kind {
     LRS_KERNEL_SCAN = 1,       /* exclusive scan of the count matrix */
     LRS_KERNEL_DOWNSWEEP = 2,  /* stable in-tile rank and scatter */
     LRS_KERNEL_COPY = 3,       /* plain device copy */
-    LRS_KERNEL_FINALIZE = 4    /* after the last pass: moves data to the output
+    LRS_KERNEL_FINALIZE = 4,   /* after the last pass: moves data to the output
                                   if skipped passes left it elsewhere */
+    LRS_KERNEL_TINY = 5        /* a whole small sort in one workgroup */
 } lrs_kernel_kind;
 
 /* Starts recording with room for `capacity` kernel launches (events are

@@ -23,7 +23,7 @@ LRS_ERR_INVALID_ARG = 1
 LRS_ERR_TEMP_TOO_SMALL = 2
 LRS_ERR_HIP = 3
 
-KERNEL_NAMES = {0: "upsweep", 1: "scan", 2: "downsweep", 3: "copy", 4: "finalize"}
+KERNEL_NAMES = {0: "upsweep", 1: "scan", 2: "downsweep", 3: "copy", 4: "finalize", 5: "tiny"}
 
 KEY_TYPES = ("u32", "i32", "f32", "u64", "i64", "f64")
 SORT_FUNCTIONS = tuple("lrs_sort_keys_" + t for t in KEY_TYPES) + tuple("lrs_sort_pairs_" + t for t in KEY_TYPES)

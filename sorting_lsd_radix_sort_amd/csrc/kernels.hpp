@@ -217,42 +217,17 @@ __device__ __forceinline__ int pass_dest(int src, int planned, bool last, bool s
 
 // -------------------------------------------------------------------- upsweep
 
-// Counts the digits of block b = keys [b * block_len, min(n, (b+1) * block_len)).
-// Each wave adds into its own LDS sub-histograms, so atomics only contend
-// within a wave (the kwkr.cn essay, section 3.2, and the quant67.com survey,
-// section 8.1: per-block and per-warp counting instead of global atomics).
-// The keys are read 16 bytes per lane when their array is 16-byte aligned.
-template <typename K, int CODE, int THREADS>
-__global__ __launch_bounds__(THREADS) void upsweep_kernel(
-    SortBufs bufs, const uint32_t *__restrict__ route, int pass, int src_fixed, uint32_t *__restrict__ counts,
-    int64_t n, int64_t block_len, int num_blocks, int shift, uint32_t mask)
+// Adds the digits of keys [begin, end) into the LDS histogram h (atomics),
+// THREADS lanes striding together.  16-byte loads, UNROLL in flight per lane,
+// where the array and `begin` are 16-byte aligned; single keys otherwise.
+template <typename K, int CODE, int THREADS, int UNROLL = 4>
+__device__ __forceinline__ void count_range(const K *__restrict__ keys, int64_t begin, int64_t end,
+                                            uint32_t *h, int tid, int shift, uint32_t mask)
 {
-    const K *__restrict__ keys = (const K *)bufs.keys[pass_source(route, pass, src_fixed)];
-    constexpr int WAVES = THREADS / kWave;
-    // COPIES sub-histograms per wave (lane % COPIES picks one), padded by one
-    // word so that equal digits in different copies fall in different banks:
-    // skewed digits then serialize at most 64/COPIES lanes per atomic.
-    constexpr int COPIES = 4;
-    constexpr int STRIDE = kRadix + 1;
-    __shared__ uint32_t hist[WAVES * COPIES][STRIDE];
-    const int tid = threadIdx.x;
-    uint32_t *h = hist[(tid / kWave) * COPIES + (tid % COPIES)];
-    for (int i = tid; i < WAVES * COPIES * STRIDE; i += THREADS) (&hist[0][0])[i] = 0u;
-    __syncthreads();
-
-    const int64_t begin = (int64_t)blockIdx.x * block_len;
-    const int64_t end = begin + block_len < n ? begin + block_len : n;
-
-    auto count_key = [&](K k) {
-        atomicAdd(&h[digit_of<CODE>(k, shift, mask)], 1u);
-    };
-
+    auto count_key = [&](K k) { atomicAdd(&h[digit_of<CODE>(k, shift, mask)], 1u); };
+    constexpr int PER = 16 / (int)sizeof(K);
     int64_t scalar_from = begin;
-    if (((uintptr_t)keys & 15) == 0) {
-        // 16-byte vectors: 4 uint32 or 2 uint64 keys each.  `begin` is a whole
-        // number of tiles, hence of vectors.
-        constexpr int PER = 16 / (int)sizeof(K);
-        constexpr int UNROLL = 4;
+    if ((((uintptr_t)keys & 15) == 0) && begin % PER == 0) {
         using V = uint4;
         const V *vk = reinterpret_cast<const V *>(keys);
         const int64_t vbeg = begin / PER, vend = end / PER;
@@ -283,6 +258,36 @@ __global__ __launch_bounds__(THREADS) void upsweep_kernel(
         scalar_from = vend * PER;
     }
     for (int64_t i = scalar_from + tid; i < end; i += THREADS) count_key(__builtin_nontemporal_load(&keys[i]));
+}
+
+
+// Counts the digits of block b = keys [b * block_len, min(n, (b+1) * block_len)).
+// Each wave adds into its own LDS sub-histograms, so atomics only contend
+// within a wave (the kwkr.cn essay, section 3.2, and the quant67.com survey,
+// section 8.1: per-block and per-warp counting instead of global atomics).
+// The keys are read 16 bytes per lane when their array is 16-byte aligned.
+template <typename K, int CODE, int THREADS>
+__global__ __launch_bounds__(THREADS) void upsweep_kernel(
+    SortBufs bufs, const uint32_t *__restrict__ route, int pass, int src_fixed, uint32_t *__restrict__ counts,
+    int64_t n, int64_t block_len, int num_blocks, int shift, uint32_t mask)
+{
+    const K *__restrict__ keys = (const K *)bufs.keys[pass_source(route, pass, src_fixed)];
+    constexpr int WAVES = THREADS / kWave;
+    // COPIES sub-histograms per wave (lane % COPIES picks one), padded by one
+    // word so that equal digits in different copies fall in different banks:
+    // skewed digits then serialize at most 64/COPIES lanes per atomic.
+    constexpr int COPIES = 4;
+    constexpr int STRIDE = kRadix + 1;
+    __shared__ uint32_t hist[WAVES * COPIES][STRIDE];
+    const int tid = threadIdx.x;
+    uint32_t *h = hist[(tid / kWave) * COPIES + (tid % COPIES)];
+    for (int i = tid; i < WAVES * COPIES * STRIDE; i += THREADS) (&hist[0][0])[i] = 0u;
+    __syncthreads();
+
+    const int64_t begin = (int64_t)blockIdx.x * block_len;
+    const int64_t end = begin + block_len < n ? begin + block_len : n;
+
+    count_range<K, CODE, THREADS>(keys, begin, end, h, tid, shift, mask);
     __syncthreads();
 
     for (int d = tid; d < kRadix; d += THREADS) {
@@ -441,43 +446,46 @@ __global__ __launch_bounds__(WAVES * kWave) void downsweep_kernel(
     const int64_t blk_end = blk_begin + block_len < n ? blk_begin + block_len : n;
     const uint32_t n32 = (uint32_t)n;
 
-    // Routing of this pass, and whether it is skipped: it is when one digit
-    // holds every key (each wave tests the 256 totals itself, so the decision
-    // is uniform without a barrier).
+    // Routing of this pass.
     const int ksrc = pass_source(route_k, pass, ksrc_fixed);
     const int vsrc = PAIRS ? pass_source(route_v, pass, vsrc_fixed) : 0;
-    bool skip;
-    {
-        const uint4 t = reinterpret_cast<const uint4 *>(row_total)[lane];
-        skip = __ballot(t.x == n32 || t.y == n32 || t.z == n32 || t.w == n32) != 0;
+    const K *__restrict__ keys_in = (const K *)bufs.keys[ksrc];
+
+    // Digit totals (4 digits per lane) and, for wave 0, this block's prefix
+    // within each digit.  The upsweep counted each block as `split`
+    // consecutive sub-blocks (count_cols columns in all): the block's prefix
+    // is the one of its first sub-block.
+    const uint4 tot4 = reinterpret_cast<const uint4 *>(row_total)[lane];
+    uint4 before4 = make_uint4(0u, 0u, 0u, 0u);
+    if (wave == 0) {
+        const int d0 = 4 * lane;
+        const int64_t col = (int64_t)blk * split;
+        before4.x = counts[(int64_t)(d0 + 0) * count_cols + col];
+        before4.y = counts[(int64_t)(d0 + 1) * count_cols + col];
+        before4.z = counts[(int64_t)(d0 + 2) * count_cols + col];
+        before4.w = counts[(int64_t)(d0 + 3) * count_cols + col];
     }
+
+    // The pass is skipped when one digit holds every key (every wave tests the
+    // totals itself, so the decision is uniform without a barrier).
+    const bool skip = __ballot(tot4.x == n32 || tot4.y == n32 || tot4.z == n32 || tot4.w == n32) != 0;
     const int kdst = pass_dest(ksrc, kplanned, last != 0, skip);
     const int vdst = PAIRS ? pass_dest(vsrc, vplanned, last != 0, skip) : 0;
     if (blk == 0 && tid == 0) {
         route_k[pass + 1] = (uint32_t)kdst;
         if constexpr (PAIRS) route_v[pass + 1] = (uint32_t)vdst;
     }
-    const K *__restrict__ keys_in = (const K *)bufs.keys[ksrc];
     K *__restrict__ keys_out = (K *)bufs.keys[kdst];
     const uint32_t *__restrict__ vals_in = PAIRS ? bufs.vals[vsrc] : nullptr;
     uint32_t *__restrict__ vals_out = PAIRS ? (uint32_t *)bufs.vals[vdst] : nullptr;
     if (skip) return;  // nothing to reorder
 
     if (wave == 0) {
-        // digit starts (exclusive prefix of the row totals), plus this block's
-        // exclusive prefix within each digit's row.  The upsweep counted each
-        // block as `split` consecutive sub-blocks (count_cols columns in all),
-        // so the block's prefix is the one of its first sub-block.
-        const uint4 tot = reinterpret_cast<const uint4 *>(row_total)[lane];
-        const uint4 start = wave_scan_digits(tot);
-        const int d0 = 4 * lane;
-        const int64_t col = (int64_t)blk * split;
-        uint4 r;
-        r.x = start.x + counts[(int64_t)(d0 + 0) * count_cols + col];
-        r.y = start.y + counts[(int64_t)(d0 + 1) * count_cols + col];
-        r.z = start.z + counts[(int64_t)(d0 + 2) * count_cols + col];
-        r.w = start.w + counts[(int64_t)(d0 + 3) * count_cols + col];
-        reinterpret_cast<uint4 *>(s.run)[lane] = r;
+        // next global index of each digit in this block: digit start
+        // (exclusive prefix of the totals) plus the block's prefix
+        const uint4 start = wave_scan_digits(tot4);
+        reinterpret_cast<uint4 *>(s.run)[lane] =
+            make_uint4(start.x + before4.x, start.y + before4.y, start.z + before4.z, start.w + before4.w);
     }
 
     // Makes the compiler wait here for a buffer's loads.
@@ -688,6 +696,98 @@ __global__ __launch_bounds__(WAVES * kWave) void downsweep_kernel(
         __syncthreads();
         if constexpr (SUB == 2) store_full(0);
         store_last(SUB - 1, (int)(blk_end - ta - TILE));
+    }
+}
+
+// ---------------------------------------------------------------- tiny sorts
+//
+// A sort of at most NMAX keys in one launch and one workgroup, with the keys
+// (and values) held in LDS for all passes: below some tens of thousands of
+// keys a sort is dominated by launch latency (the page "GPU radix sort: from
+// the CUB implementation to performance tuning", sections 1 and 6), and this
+// takes one launch instead of three per pass.  The 16 waves each own a
+// contiguous segment of the keys.  Per pass: each wave counts the digits of its
+// segment; wave 0 turns the (digit, wave) counts into every wave's first slot
+// per digit; then each wave walks its segment in input order, 64 keys at a
+// time, ranking them with the ballot match and its own running offsets.  The
+// walk needs no barrier, and equal digits keep input order: earlier waves hold
+// earlier segments, and a wave ranks its keys in order.
+template <typename K, bool PAIRS, int CODE, int NMAX>
+__global__ __launch_bounds__(1024) void tiny_sort_kernel(const K *__restrict__ keys_in,
+                                                        const uint32_t *__restrict__ vals_in,
+                                                        K *__restrict__ keys_out, uint32_t *__restrict__ vals_out,
+                                                        int n, int begin_bit, int end_bit)
+{
+    constexpr int THREADS = 1024, WAVES = THREADS / kWave;
+    __shared__ K sk[2][NMAX];
+    __shared__ uint32_t sv[PAIRS ? 2 : 1][PAIRS ? NMAX : 1];
+    __shared__ alignas(16) uint32_t off[WAVES][kRadix];  // per wave: digit counts, then next slot per digit
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+
+    for (int i = tid; i < n; i += THREADS) {
+        sk[0][i] = keys_in[i];
+        if constexpr (PAIRS) sv[0][i] = vals_in[i];
+    }
+    const int seg = ((n + WAVES - 1) / WAVES + kWave - 1) / kWave * kWave;
+    const int sb = min(wave * seg, n), se = min(sb + seg, n);
+    __syncthreads();
+
+    int cur = 0;
+    for (int shift = begin_bit; shift < end_bit; shift += kRadixBits, cur ^= 1) {
+        const int width = min(kRadixBits, end_bit - shift);
+        const uint32_t mask = (1u << width) - 1u;
+
+        // counts of this wave's segment, in its own row
+        for (int d = lane; d < kRadix; d += kWave) off[wave][d] = 0u;
+        for (int i = sb + lane; i < se; i += kWave) atomicAdd(&off[wave][digit_of<CODE>(sk[cur][i], shift, mask)], 1u);
+        __syncthreads();
+
+        if (wave == 0) {
+            uint32_t c[4][WAVES];
+            uint4 tot = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+            for (int w = 0; w < WAVES; ++w) {
+                const uint4 x = reinterpret_cast<const uint4 *>(off[w])[lane];
+                c[0][w] = x.x; c[1][w] = x.y; c[2][w] = x.z; c[3][w] = x.w;
+                tot.x += x.x; tot.y += x.y; tot.z += x.z; tot.w += x.w;
+            }
+            uint4 run = wave_scan_digits(tot);
+#pragma unroll
+            for (int w = 0; w < WAVES; ++w) {
+                reinterpret_cast<uint4 *>(off[w])[lane] = run;
+                run.x += c[0][w]; run.y += c[1][w]; run.z += c[2][w]; run.w += c[3][w];
+            }
+        }
+        __syncthreads();
+
+        for (int base = sb; base < se; base += kWave) {
+            const int i = base + lane;
+            const bool valid = i < se;
+            const K k = valid ? sk[cur][i] : (K)0;
+            uint32_t v = 0;
+            if constexpr (PAIRS) v = valid ? sv[cur][i] : 0u;
+            const uint32_t d = digit_of<CODE>(k, shift, mask);
+            uint32_t lo, hi;
+            match_digit(d, lo, hi);
+            const uint64_t vm = __ballot(valid);
+            lo &= (uint32_t)vm;
+            hi &= (uint32_t)(vm >> 32);
+            const uint32_t below = lanes_below(lo, hi);
+            const uint32_t same = __popc(lo) + __popc(hi);
+            uint32_t *counter = &off[wave][d];
+            const uint32_t slot = *counter + below;
+            if (valid) {
+                sk[cur ^ 1][slot] = k;
+                if constexpr (PAIRS) sv[cur ^ 1][slot] = v;
+                if (below + 1u == same) *counter = slot + 1u;  // the group's last lane advances it
+            }
+        }
+        __syncthreads();
+    }
+
+    for (int i = tid; i < n; i += THREADS) {
+        keys_out[i] = sk[cur][i];
+        if constexpr (PAIRS) vals_out[i] = sv[cur][i];
     }
 }
 

@@ -48,6 +48,16 @@ constexpr int kScanThreads = 256;
 constexpr int kScanPerThread = kMaxBlocks / kScanThreads;
 constexpr size_t kAlign = 256;
 
+// Sorts of at most tiny_max keys run in one launch of one workgroup with the
+// data in LDS (tiny_sort_kernel): two copies of the keys and values in 128 KB.
+template <typename K, bool PAIRS>
+constexpr int tiny_max()
+{
+    return (64 * 1024) / (int)(sizeof(K) + (PAIRS ? 4 : 0)) >= 16384 ? 16384
+           : (64 * 1024) / (int)(sizeof(K) + (PAIRS ? 4 : 0)) >= 8192 ? 8192
+                                                                       : 4096;
+}
+
 // Downsweep tile shapes (waves per workgroup x keys per lane): 8192-key
 // tiles.  The tile size sets how many keys of each digit a workgroup writes
 // in one piece (about tile/256 per tile): longer pieces leave fewer
@@ -329,6 +339,22 @@ hipError_t blocks_for(int64_t tiles, int *blocks)
     return hipSuccess;
 }
 
+// The buffers a sort's data can be in, by BufIndex.
+template <bool PAIRS>
+SortBufs sort_bufs(const Request &rq, const Layout &L, char *temp)
+{
+    SortBufs bufs;
+    bufs.keys[BUF_IN] = rq.keys_in;
+    bufs.keys[BUF_OUT] = rq.keys_out;
+    bufs.keys[BUF_A] = L.kplan.need_a ? temp + L.off_ka : nullptr;
+    bufs.keys[BUF_B] = L.kplan.need_b ? temp + L.off_kb : nullptr;
+    bufs.vals[BUF_IN] = rq.vals_in;
+    bufs.vals[BUF_OUT] = rq.vals_out;
+    bufs.vals[BUF_A] = PAIRS && L.vplan.need_a ? (const uint32_t *)(temp + L.off_va) : nullptr;
+    bufs.vals[BUF_B] = PAIRS && L.vplan.need_b ? (const uint32_t *)(temp + L.off_vb) : nullptr;
+    return bufs;
+}
+
 template <typename K, bool PAIRS, int WAVES, int ITEMS, int CODE>
 lrs_status run_passes(const Request &rq, const Layout &L, char *temp, hipStream_t stream)
 {
@@ -357,15 +383,7 @@ lrs_status run_passes(const Request &rq, const Layout &L, char *temp, hipStream_
     uint32_t *rowtot = (uint32_t *)(temp + L.off_rowtot);
     uint32_t *route_k = (uint32_t *)(temp + L.off_route);
     uint32_t *route_v = route_k + kMaxRoute;
-    SortBufs bufs;
-    bufs.keys[BUF_IN] = rq.keys_in;
-    bufs.keys[BUF_OUT] = rq.keys_out;
-    bufs.keys[BUF_A] = L.kplan.need_a ? temp + L.off_ka : nullptr;
-    bufs.keys[BUF_B] = L.kplan.need_b ? temp + L.off_kb : nullptr;
-    bufs.vals[BUF_IN] = rq.vals_in;
-    bufs.vals[BUF_OUT] = rq.vals_out;
-    bufs.vals[BUF_A] = PAIRS && L.vplan.need_a ? (const uint32_t *)(temp + L.off_va) : nullptr;
-    bufs.vals[BUF_B] = PAIRS && L.vplan.need_b ? (const uint32_t *)(temp + L.off_vb) : nullptr;
+    const SortBufs bufs = sort_bufs<PAIRS>(rq, L, temp);
     // An in-place array starts in the output buffer (the same memory).
     const int kstart = rq.keys_in == rq.keys_out ? BUF_OUT : BUF_IN;
     const int vstart = PAIRS && rq.vals_in == rq.vals_out ? BUF_OUT : BUF_IN;
@@ -399,9 +417,22 @@ lrs_status run_passes(const Request &rq, const Layout &L, char *temp, hipStream_
     return err == hipSuccess ? LRS_OK : LRS_ERR_HIP;
 }
 
+template <typename K, bool PAIRS, int CODE>
+lrs_status run_tiny(const Request &rq, hipStream_t stream)
+{
+    constexpr int NMAX = tiny_max<K, PAIRS>();
+    const hipError_t err = launch(LRS_KERNEL_TINY, stream, [&] {
+        tiny_sort_kernel<K, PAIRS, CODE, NMAX><<<1, 1024, 0, stream>>>(
+            (const K *)rq.keys_in, rq.vals_in, (K *)rq.keys_out, rq.vals_out, (int)rq.n, rq.begin_bit, rq.end_bit);
+    });
+    return err == hipSuccess ? LRS_OK : LRS_ERR_HIP;
+}
+
 template <typename K, int CODE>
 lrs_status run_kind(bool pairs, const Request &r, const Layout &L, char *temp, hipStream_t stream)
 {
+    if (pairs && r.n <= tiny_max<K, true>()) return run_tiny<K, true, CODE>(r, stream);
+    if (!pairs && r.n <= tiny_max<K, false>()) return run_tiny<K, false, CODE>(r, stream);
     constexpr int W = sizeof(K) == 8 ? kWaves64 : kWaves32;
     constexpr int I = sizeof(K) == 8 ? kItems64 : kItems32;
     if (pairs) return run_passes<K, true, W, I, CODE>(r, L, temp, stream);

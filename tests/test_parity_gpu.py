@@ -25,6 +25,9 @@ from sorting_lsd_radix_sort_amd import inputs
 pytestmark = pytest.mark.gpu
 
 TILE = 8192  # keys per downsweep tile
+BIG_N = 1 << 17  # above every single-workgroup size limit: the multi-kernel path
+# largest n sorted by one workgroup in LDS, per (key bytes, pairs)
+TINY_MAX = {(4, False): 16384, (4, True): 8192, (8, False): 8192, (8, True): 4096}
 SMALL_SIZES = [0, 1, 2, 3, 63, 64, 65, 255, 256, 257, 1023, 1024, 1025, 4095, 4096, 4097,
                TILE - 1, TILE, TILE + 1, 2 * TILE, 3 * TILE + 17, 65_536]
 RANGES = {"u32": [(0, 32), (0, 20), (8, 16), (3, 17), (31, 32), (24, 32), (5, 5)],
@@ -68,8 +71,8 @@ def test_small_sizes_all_ranges(key_type, pairs):
                                            ("u32", "dup"), ("f32", "uniform"), ("i32", "and3"),
                                            ("i32", "uniform"), ("i64", "dup"), ("i64", "uniform"),
                                            ("f64", "fmix"), ("f64", "uniform")])
-def test_skewed_and_special_values(key_type, dist):
-    n = 5 * TILE + 1234
+@pytest.mark.parametrize("n", [5 * TILE + 1234, BIG_N + 5 * TILE + 1234])
+def test_skewed_and_special_values(key_type, dist, n):
     keys = inputs.random_keys(key_type, n, 77, dist)
     for pairs in (False, True):
         vals = np.random.default_rng(5).permutation(n).astype(np.uint32) if pairs else None
@@ -110,8 +113,8 @@ def test_multi_tile_blocks_vs_oracle(key_type, n, pairs):
 # ------------------------------------------------------------------ in-place use
 
 @pytest.mark.parametrize("key_type", KEY_TYPES)
-def test_in_place(key_type):
-    n = 3 * TILE + 101
+@pytest.mark.parametrize("n", [3 * TILE + 101, BIG_N + 3 * TILE + 101])
+def test_in_place(key_type, n):
     keys = inputs.random_keys(key_type, n, 9, "fmix" if key_type in ("f32", "f64") else "dup")
     vals = np.random.default_rng(3).permutation(n).astype(np.uint32)
     bits = 8 * keys.dtype.itemsize
@@ -238,7 +241,7 @@ def test_constant_digit_passes_vs_oracle(digits, pairs):
     sits elsewhere than planned, later passes and the final copy follow it.
     Covers skipped first, middle and last passes, odd and even numbers of skips
     before a pass that runs, and all passes skipped."""
-    n = 5 * TILE + 777
+    n = BIG_N + 5 * TILE + 777  # passes are skipped on the multi-kernel path
     base = inputs.random_keys("u32", n, 123, "uniform")
     keys = _with_constant_digits(base, digits, 32)
     vals = np.random.default_rng(4).permutation(n).astype(np.uint32) if pairs else None
@@ -252,7 +255,7 @@ def test_constant_digit_passes_vs_oracle(digits, pairs):
 
 @pytest.mark.parametrize("key_type", ["u64", "f32", "i64"])
 def test_constant_digit_passes_other_types(key_type):
-    n = 3 * TILE + 55
+    n = BIG_N + 3 * TILE + 55
     base = inputs.random_keys(key_type, n, 7, "uniform")
     bits = 8 * base.dtype.itemsize
     for digits in [(1,), (bits // 8 - 1,), (0, 2, 4), tuple(range(bits // 8))]:
@@ -261,3 +264,28 @@ def test_constant_digit_passes_other_types(key_type):
         announce("constant digits %s %s" % (digits, key_type))
         _compare(keys, vals, 0, bits)
         _compare(keys, vals, 0, bits, in_place_keys=True, in_place_vals=True)
+
+
+@pytest.mark.parametrize("key_type", ["u32", "f32", "u64", "f64"])
+@pytest.mark.parametrize("pairs", [False, True])
+def test_tiny_path_boundary(key_type, pairs):
+    """Sizes on both sides of the single-workgroup limit, constant keys, and
+    in-place use on the single-workgroup path."""
+    ksz = np.dtype(inputs.KEY_DTYPES[key_type]).itemsize
+    lim = TINY_MAX[(ksz, pairs)]
+    bits = 8 * ksz
+    for n in (lim - 1, lim, lim + 1, 2 * lim + 3):
+        keys = inputs.random_keys(key_type, n, 5, "uniform")
+        vals = np.arange(n, dtype=np.uint32) if pairs else None
+        announce("tiny boundary %s pairs=%s n=%d" % (key_type, pairs, n))
+        _compare(keys, vals, 0, bits)
+        _compare(keys, vals, 3, bits - 5)
+    n = lim - 3
+    keys = np.full(n, 7, dtype=inputs.KEY_DTYPES[key_type])
+    vals = np.arange(n, dtype=np.uint32) if pairs else None
+    announce("tiny constant keys %s pairs=%s" % (key_type, pairs))
+    _compare(keys, vals, 0, bits)
+    keys = inputs.random_keys(key_type, n, 8, "dup")
+    for b, e in [(0, 8), (0, 16), (0, 24), (4, 9)]:
+        announce("tiny in-place %s pairs=%s bits=[%d,%d)" % (key_type, pairs, b, e))
+        _compare(keys, vals, b, e, in_place_keys=True, in_place_vals=pairs)
