@@ -77,7 +77,12 @@ __device__ __forceinline__ K order_code(K k)
 template <int CODE, typename K>
 __device__ __forceinline__ uint32_t digit_of(K k, int shift, uint32_t mask)
 {
-    return (uint32_t)(order_code<K, CODE>(k) >> shift) & mask;
+    if constexpr (sizeof(K) == 4) {
+        // one bitfield extract (mask is 2^width - 1, the same for all lanes)
+        return __builtin_amdgcn_ubfe((uint32_t)order_code<K, CODE>(k), (uint32_t)shift, (uint32_t)__popc(mask));
+    } else {
+        return (uint32_t)(order_code<K, CODE>(k) >> shift) & mask;
+    }
 }
 
 // A key whose code is all ones: its digit is the largest of any pass, so the
@@ -332,22 +337,36 @@ __global__ __launch_bounds__(THREADS) void scan_kernel(uint32_t *__restrict__ co
 }
 
 // ------------------------------------------------------------------ downsweep
-
-template <typename K, bool PAIRS, int WAVES, int ITEMS, int SUB>
-struct DownsweepSmem {
-    static constexpr int kThreads = WAVES * kWave;
-    static constexpr int kTile = kThreads * ITEMS;
-    K keys[SUB][kTile];                                 // SUB tiles, each in digit order
-    uint32_t vals[PAIRS ? SUB : 1][PAIRS ? kTile : 1];  // payload in the same order
-    // Per-wave 16-bit digit counters, two buffers alternating by tile: the
-    // current tile counts in one; in the other, each wave's own row holds its
-    // slot bases (tile slot of its first key of digit d) for the scatter.
-    alignas(16) uint16_t wave_count[2][WAVES][kRadix];
-    alignas(16) uint32_t out_base[SUB][kRadix];         // global index of tile slot 0 of digit d
-    alignas(16) uint32_t run[kRadix];                   // next global index of digit d in this block
-    uint16_t sink[WAVES][kWave];                        // stores of non-leader lanes land here
-};
-
+//
+// Stable rank and scatter of one digit, one workgroup per block (a contiguous
+// run of tiles).  Tile layout: wave w owns keys [w*64*ITEMS, (w+1)*64*ITEMS)
+// of the tile, item i of lane l is key w*64*ITEMS + i*64 + l, so each load
+// instruction reads 64 consecutive keys and (item, lane) order is input order.
+// Per tile: each wave ranks its keys among its own keys of the same digit
+// (per-wave 16-bit counters in LDS, 64-lane match masks within an item), the
+// waves' counts give every key its slot in the tile in digit order, the keys
+// are written to LDS at those slots, and the tile is stored from LDS with
+// consecutive threads on consecutive slots, so each digit's run goes out as
+// consecutive addresses.
+//
+// Write combining.  A digit's run from one tile starts and ends inside 128-byte
+// output lines.  Stored as is, the line it shares with the same digit's run
+// from the next tile reaches HBM as two partial writes a tile apart, and
+// partial line writes cost far more than their bytes (both in this kernel and
+// in the next pass's reads of the lines).  So each workgroup holds, for every
+// digit, the keys of the output line its run has opened but not filled (the
+// carry: LINE positions per digit), and a tile stores only the carry keys and
+// tile keys that complete a line.  The lines at the two ends of a block's range
+// of a digit are shared with the neighbouring blocks and go out in parts; every
+// other line is written whole, once.  The carry is in LDS for 32-bit keys
+// alone and in registers otherwise (where the tile's LDS already allows only
+// one workgroup per CU).
+//
+// Stores are buffer stores (outputs up to 2 GiB): a lane with nothing to store
+// gives an offset past the output buffer, which the buffer's range check drops.
+// No store sits in a branch, every path issues the same memory operations, and
+// the wait for the next tile's loads is counted exactly.  WIDE outputs use
+// plain stores under a branch instead.
 // Buffer resource over `bytes` bytes from `base`: buffer loads through it at
 // byte offsets at or past `bytes` return zero without touching memory.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_over(const void *base, uint32_t bytes)
@@ -402,40 +421,120 @@ __device__ __forceinline__ void finish_tile(K (&k)[ITEMS], int first, int valid,
     }
 }
 
-// Stable rank + scatter of block b's tiles for one digit.  Tile layout: wave w
-// owns keys [w*64*ITEMS, (w+1)*64*ITEMS) of the tile, item i of lane l is key
-// w*64*ITEMS + i*64 + l, so each load instruction reads 64 consecutive keys and
-// (item, lane) order is input order.
-//
-// Tiles are taken two at a time, A and B, in two register buffers: while A is
-// ranked, B's keys load into the second buffer, and while B is ranked, the next
-// A's keys load into the first.  Unrolled this way the buffers stay in fixed
-// registers across the loop, with no copy at the loop head of a buffer whose
-// loads may still be in flight, so each wait for a prefetch sits where it is
-// placed below: before the tile that uses it, and always before a flush's
-// stores (the memory counter is in order, so a wait issued after stores would
-// wait for the stores too).
-//
-// SUB (1 or 2) consecutive tiles are ranked and reordered into SUB LDS regions
-// before they are written out together.  A digit's runs from consecutive tiles
-// are adjacent in the output, so the output line they share is completed by two
-// stores issued back to back (merged in L2) instead of one tile apart: the
-// store stream behaves like runs SUB times longer, with the registers of one
-// tile.
-template <typename K, bool PAIRS, int WAVES, int ITEMS, int SUB, int CODE>
-__global__ __launch_bounds__(WAVES * kWave) void downsweep_kernel(
-    SortBufs bufs, uint32_t *__restrict__ route_k, uint32_t *__restrict__ route_v, int pass, int ksrc_fixed,
-    int vsrc_fixed, int kplanned, int vplanned, int last, const uint32_t *__restrict__ counts,
-    const uint32_t *__restrict__ row_total, int64_t n, int64_t block_len, int count_cols, int split, int shift,
-    uint32_t mask)
+constexpr uint32_t kStoreNowhere = 0x80000000u;  // byte offset past every narrow output buffer
+
+template <typename K>
+__device__ __forceinline__ void buffer_store(K x, __amdgpu_buffer_rsrc_t r, uint32_t off);
+template <>
+__device__ __forceinline__ void buffer_store<uint32_t>(uint32_t x, __amdgpu_buffer_rsrc_t r, uint32_t off)
 {
-    using Smem = DownsweepSmem<K, PAIRS, WAVES, ITEMS, SUB>;
+    __builtin_amdgcn_raw_buffer_store_b32(x, r, off, 0, 0);
+}
+template <>
+__device__ __forceinline__ void buffer_store<uint64_t>(uint64_t x, __amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    u32x2 v;
+    v[0] = (uint32_t)x;
+    v[1] = (uint32_t)(x >> 32);
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+}
+
+// Stores x at element `pos` of the output when `put`.
+template <bool WIDE, typename T>
+__device__ __forceinline__ void store_out(T x, T *out, __amdgpu_buffer_rsrc_t r, uint32_t pos, bool put)
+{
+    if constexpr (WIDE) {
+        if (put) out[pos] = x;
+    } else {
+        buffer_store<T>(x, r, put ? pos * (uint32_t)sizeof(T) : kStoreNowhere);
+    }
+}
+
+// Bits [a, b) of a lane mask, for 0 <= a and b <= 31 (empty when a >= b).
+__device__ __forceinline__ uint32_t bit_range(uint32_t a, uint32_t b)
+{
+    return ((1u << b) - 1u) & ~((1u << a) - 1u);
+}
+
+// The lanes of the wave whose digit equals this lane's, through LDS: every
+// lane clears its digit's 64-bit slot of the wave's table, sets its own bit
+// there (an atomic OR, so the order of lanes does not matter) and reads the
+// slot back.  DS operations of one wave complete in issue order, so the read
+// sees every lane's bit.  Three LDS operations instead of the ballot form's 32
+// VALU instructions; the rank loop alternates the two forms so that neither
+// the VALU nor the LDS pipe carries all of the matching.
+__device__ __forceinline__ void match_digit_lds(unsigned long long *slot, unsigned long long lane_bit,
+                                                uint32_t &lo, uint32_t &hi)
+{
+    *slot = 0ull;
+    atomicOr(slot, lane_bit);
+    const unsigned long long m = *slot;
+    lo = (uint32_t)m;
+    hi = (uint32_t)(m >> 32);
+}
+
+template <typename K, bool PAIRS>
+constexpr bool carry_in_lds()
+{
+    return sizeof(K) == 4 && !PAIRS;
+}
+
+// Waves per SIMD the register allocation has to allow: 32-bit keys alone run
+// 16 waves per CU (LDS allows it); the other shapes run 8.
+template <typename K, bool PAIRS>
+constexpr int downsweep_waves_per_simd()
+{
+    return carry_in_lds<K, PAIRS>() ? 4 : 2;
+}
+
+template <typename K, bool PAIRS, int WAVES, int ITEMS>
+struct DownsweepSmem {
+    static constexpr int kThreads = WAVES * kWave;
+    static constexpr int kTile = kThreads * ITEMS;
+    static constexpr bool kCarryLds = carry_in_lds<K, PAIRS>();
+    // Output line, in positions: 128 bytes of keys; with values, 128 bytes of
+    // values (and 128 or 256 of keys).
+    static constexpr uint32_t kLine = PAIRS ? 32u : 128u / (uint32_t)sizeof(K);
+    K keys[kTile];                     // the tile in digit order
+    uint32_t vals[PAIRS ? kTile : 1];  // payload in the same order
+    // The carry, when in LDS: lane e of digit d holds output index (open line
+    // of d) + e.
+    K carry[kCarryLds ? kRadix : 1][kCarryLds ? kLine : 1];
+    // Per-wave 16-bit digit counters, two buffers alternating by tile: the
+    // current tile counts in one; in the other, each wave's own row holds its
+    // slot bases (tile slot of its first key of digit d) for the scatter.
+    alignas(16) uint16_t wave_count[2][WAVES][kRadix];
+    alignas(16) unsigned long long match_table[WAVES][kRadix];  // per-wave slots of match_digit_lds
+    // Per digit d: {output index of tile slot 0 of d, end of the indices
+    // stored from the tile}.
+    alignas(16) uint2 place[kRadix];
+    // Per digit d: {output index of d's open line, carry lanes to store} and,
+    // for a carry in registers, {tile slot of the line left open after the
+    // tile, carry lanes to reload from the tile}.
+    alignas(16) std::conditional_t<kCarryLds, uint2, uint4> pend[kRadix];
+    alignas(16) uint32_t run[kRadix];    // next output index of digit d in this block
+    alignas(16) uint32_t start[kRadix];  // first output index of digit d in this block
+};
+
+template <typename K, bool PAIRS, int WAVES, int ITEMS, int CODE, bool WIDE>
+__global__ __launch_bounds__(WAVES *kWave)
+    __attribute__((amdgpu_waves_per_eu(downsweep_waves_per_simd<K, PAIRS>()))) void downsweep_kernel(
+        SortBufs bufs, uint32_t *__restrict__ route_k, uint32_t *__restrict__ route_v, int pass, int ksrc_fixed,
+        int vsrc_fixed, int kplanned, int vplanned, int last, const uint32_t *__restrict__ counts,
+        const uint32_t *__restrict__ row_total, int64_t n, int64_t block_len, int count_cols, int split, int shift,
+        uint32_t mask)
+{
+    using Smem = DownsweepSmem<K, PAIRS, WAVES, ITEMS>;
     constexpr int THREADS = Smem::kThreads;
     constexpr int TILE = Smem::kTile;
     constexpr int WAVE_KEYS = kWave * ITEMS;
+    constexpr uint32_t LINE = Smem::kLine;
+    constexpr bool CARRY_LDS = Smem::kCarryLds;
+    constexpr int CARRY = (int)(kRadix * LINE) / THREADS;  // carry positions per thread
     static_assert(THREADS >= kRadix, "one thread per digit is assumed");
-    static_assert(TILE < 65536, "ranks and counters are 16-bit");
-    static_assert(SUB == 1 || SUB == 2, "one or two tiles per flush");
+    static_assert(TILE < 65536 && (TILE & (TILE - 1)) == 0, "16-bit ranks, power-of-two tile");
+    static_assert(THREADS % LINE == 0 && (kRadix * LINE) % THREADS == 0, "carry lanes map evenly");
     __shared__ Smem s;
 
     const int tid = threadIdx.x;
@@ -475,17 +574,19 @@ __global__ __launch_bounds__(WAVES * kWave) void downsweep_kernel(
         route_k[pass + 1] = (uint32_t)kdst;
         if constexpr (PAIRS) route_v[pass + 1] = (uint32_t)vdst;
     }
+    if (skip) return;  // nothing to reorder
     K *__restrict__ keys_out = (K *)bufs.keys[kdst];
     const uint32_t *__restrict__ vals_in = PAIRS ? bufs.vals[vsrc] : nullptr;
     uint32_t *__restrict__ vals_out = PAIRS ? (uint32_t *)bufs.vals[vdst] : nullptr;
-    if (skip) return;  // nothing to reorder
 
+    // The block's first output index of each digit (digit start plus the
+    // block's prefix); wave 0 alone reads and advances these.
     if (wave == 0) {
-        // next global index of each digit in this block: digit start
-        // (exclusive prefix of the totals) plus the block's prefix
         const uint4 start = wave_scan_digits(tot4);
-        reinterpret_cast<uint4 *>(s.run)[lane] =
+        const uint4 first =
             make_uint4(start.x + before4.x, start.y + before4.y, start.z + before4.z, start.w + before4.w);
+        reinterpret_cast<uint4 *>(s.run)[lane] = first;
+        reinterpret_cast<uint4 *>(s.start)[lane] = first;
     }
 
     // Makes the compiler wait here for a buffer's loads.
@@ -506,11 +607,13 @@ __global__ __launch_bounds__(WAVES * kWave) void downsweep_kernel(
 
     // The block's keys and values, as buffers: loads past the block's end
     // read zero.  A block holds at most 2^31 bytes of keys (the host keeps
-    // blocks below that).
+    // blocks below that).  The outputs as buffers (used unless WIDE).
     const __amdgpu_buffer_rsrc_t keys_buf =
         buffer_over(keys_in + blk_begin, (uint32_t)((blk_end - blk_begin) * (int64_t)sizeof(K)));
     const __amdgpu_buffer_rsrc_t vals_buf =
         buffer_over(PAIRS ? vals_in + blk_begin : nullptr, PAIRS ? (uint32_t)((blk_end - blk_begin) * 4) : 0u);
+    const __amdgpu_buffer_rsrc_t kout_buf = buffer_over(keys_out, WIDE ? 0u : (uint32_t)(n * (int64_t)sizeof(K)));
+    const __amdgpu_buffer_rsrc_t vout_buf = buffer_over(vals_out, PAIRS && !WIDE ? n32 * 4u : 0u);
 
     // Issues the loads of the block's tile at tile_begin into kb.  The same
     // loads are issued whether or not the tile exists (past the block's end
@@ -521,12 +624,24 @@ __global__ __launch_bounds__(WAVES * kWave) void downsweep_kernel(
         issue_tile_loads<K, ITEMS>(kb, keys_buf, (uint32_t)(tile_begin - blk_begin), lane_first());
     };
 
-    // Ranks the tile at tile_begin, whose keys are in kb, into LDS region
-    // `sub`.  `par` selects the counter buffer (tile parity in the block).
-    auto rank_tile = [&](K(&kb)[ITEMS], int64_t tile_begin, int sub, int par) {
+    // A carry in registers: thread t holds positions (i*THREADS + t) % LINE
+    // of digit (i*THREADS + t) / LINE, for i < CARRY.
+    K ck[CARRY_LDS ? 1 : CARRY];
+    uint32_t cv[PAIRS ? CARRY : 1];
+#pragma unroll
+    for (int i = 0; i < (CARRY_LDS ? 1 : CARRY); ++i) ck[i] = (K)0;
+#pragma unroll
+    for (int i = 0; i < (PAIRS ? CARRY : 1); ++i) cv[i] = 0u;
+
+    // Ranks the tile at tile_begin (keys in kb) into LDS and writes out what it
+    // completes.  `par` selects the counter buffer (tile parity in the block);
+    // `final_tile` is set for the block's last tile, which also writes the
+    // lines it leaves open.
+    auto process_tile = [&](K(&kb)[ITEMS], int64_t tile_begin, int par, bool final_tile) {
         const int valid = blk_end - tile_begin < TILE ? (int)(blk_end - tile_begin) : TILE;
         const bool full = valid == TILE;
         const int first = lane_first();
+        const unsigned long long lane_bit = 1ull << lane;
         uint32_t v[ITEMS];
         if constexpr (PAIRS) issue_tile_loads<uint32_t, ITEMS>(v, vals_buf, (uint32_t)(tile_begin - blk_begin), first);
         finish_tile<K, CODE, ITEMS>(kb, first, valid, full);
@@ -542,12 +657,12 @@ __global__ __launch_bounds__(WAVES * kWave) void downsweep_kernel(
         reinterpret_cast<uint2 *>(count[wave])[lane] = make_uint2(0u, 0u);
 
         // Rank within the wave: keys of earlier items (all lanes), then keys of
-        // this item in lower lanes with the same digit.  The last lane of each
-        // same-digit group advances the wave's counter for that digit; the other
-        // lanes store into their own sink word, so there is no branch.
-        // The counter read is issued before the ballots so its latency hides
-        // under them; the scheduling fence keeps the compiler from hoisting
-        // every item's bit masks at once (which costs registers, not time).
+        // this item in lower lanes with the same digit.  Every lane of a
+        // same-digit group writes the group's new count (the same value), so
+        // no lane has to be picked to do it.  The counter read is issued
+        // before the match so its latency hides under it; the scheduling
+        // fence keeps the compiler from hoisting every item's match at once
+        // (which costs registers, not time).
         uint32_t r[ITEMS];
 #pragma unroll
         for (int i = 0; i < ITEMS; ++i) {
@@ -555,147 +670,188 @@ __global__ __launch_bounds__(WAVES * kWave) void downsweep_kernel(
             uint16_t *counter = &count[wave][d];
             const uint32_t prior = *counter;
             uint32_t lo, hi;
-            match_digit(d, lo, hi);
-            const uint32_t below = lanes_below(lo, hi);
-            const uint32_t same = __popc(lo) + __popc(hi);
-            uint16_t *dst = (below + 1u == same) ? counter : &s.sink[wave][lane];
-            *dst = (uint16_t)(prior + same);
-            r[i] = (d << 16) | (prior + below);  // digit and rank (< 2^16) in one register
+            if (i & 1)
+                match_digit_lds(&s.match_table[wave][d], lane_bit, lo, hi);
+            else
+                match_digit(d, lo, hi);
+            *counter = (uint16_t)(prior + __popc(lo) + __popc(hi));
+            r[i] = prior + lanes_below(lo, hi);
+            asm volatile("" : "+v"(r[i]));  // formed here, so d and the masks die here
             __builtin_amdgcn_sched_barrier(0);
         }
         __syncthreads();
 
+        // Every wave forms the digit offsets itself (4 digits per lane): its
+        // own prefix over the waves before it, and the tile's exclusive prefix
+        // over digits.  Redundant across waves, but it needs no second barrier
+        // and no wave waits for another.
+        uint4 tot = make_uint4(0u, 0u, 0u, 0u), off;
         {
-            // Every wave forms the digit offsets itself (4 digits per lane):
-            // its own prefix over the waves before it, and the tile's
-            // exclusive prefix over digits.  Redundant across waves, but it
-            // needs no second barrier and no wave waits for another.
             uint4 before = make_uint4(0u, 0u, 0u, 0u);
-            uint4 tot = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
             for (int w = 0; w < WAVES; ++w) {
                 const uint2 c = reinterpret_cast<const uint2 *>(count[w])[lane];
                 if (w == wave) before = tot;
                 tot.x += c.x & 0xFFFFu; tot.y += c.x >> 16; tot.z += c.y & 0xFFFFu; tot.w += c.y >> 16;
             }
-            const uint4 off = wave_scan_digits(tot);
+            off = wave_scan_digits(tot);
             reinterpret_cast<uint2 *>(slot_base[wave])[lane] =
                 make_uint2((before.x + off.x) | ((before.y + off.y) << 16),
                            (before.z + off.z) | ((before.w + off.w) << 16));
-            if (wave == 0) {
-                uint4 run = reinterpret_cast<const uint4 *>(s.run)[lane];
-                reinterpret_cast<uint4 *>(s.out_base[sub])[lane] =
-                    make_uint4(run.x - off.x, run.y - off.y, run.z - off.z, run.w - off.w);
-                // the padding slots of a short last tile were counted under digit `mask`
-                const uint32_t pad = (uint32_t)(TILE - valid);
-                const int d0 = 4 * lane;
-                run.x += tot.x - ((uint32_t)(d0 + 0) == mask ? pad : 0u);
-                run.y += tot.y - ((uint32_t)(d0 + 1) == mask ? pad : 0u);
-                run.z += tot.z - ((uint32_t)(d0 + 2) == mask ? pad : 0u);
-                run.w += tot.w - ((uint32_t)(d0 + 3) == mask ? pad : 0u);
-                reinterpret_cast<uint4 *>(s.run)[lane] = run;
-            }
         }
 
         // Reorder the tile in LDS: slot = tile offset of the digit + rank.
 #pragma unroll
-        for (int i = 0; i < ITEMS; ++i) r[i] = (r[i] & 0xFFFFu) + slot_base[wave][r[i] >> 16];
+        for (int i = 0; i < ITEMS; ++i) r[i] += slot_base[wave][digit_of<CODE>(kb[i], shift, mask)];
 #pragma unroll
         for (int i = 0; i < ITEMS; ++i) {
-            s.keys[sub][r[i]] = kb[i];
-            if constexpr (PAIRS) s.vals[sub][r[i]] = v[i];
+            s.keys[r[i]] = kb[i];
+            if constexpr (PAIRS) s.vals[r[i]] = v[i];
         }
-    };
 
-    // Writes LDS region t, a full tile, to the output.  Consecutive threads
-    // take consecutive slots: each digit's run of slots goes to consecutive
-    // global addresses.  With matching counts in upsweep and downsweep every
-    // dest is below n; the clamp here (and the test in the short tile) only
-    // keeps a key array changed between the two kernels by a racing caller
-    // from turning into stores outside the output.  No barrier follows: the
-    // LDS read here is next written after the next tile's rank barrier.
-    auto store_full = [&](int t) {
-        int tid_l = tid;
-        asm volatile("" : "+v"(tid_l));
+        // Wave 0 places this tile's runs and plans its stores.
+        if (wave == 0) {
+            // The padding slots of a short last tile were counted under digit
+            // `mask`; they sit after that digit's real keys and are never
+            // stored.
+            const uint32_t pad = (uint32_t)(TILE - valid);
+            const int d0 = 4 * lane;
+            const uint4 run4 = reinterpret_cast<const uint4 *>(s.run)[lane];
+            const uint4 start4 = reinterpret_cast<const uint4 *>(s.start)[lane];
+            const uint32_t lo_[4] = {run4.x, run4.y, run4.z, run4.w};
+            const uint32_t st_[4] = {start4.x, start4.y, start4.z, start4.w};
+            const uint32_t tt_[4] = {tot.x, tot.y, tot.z, tot.w};
+            const uint32_t of_[4] = {off.x, off.y, off.z, off.w};
+            uint32_t hi_[4];
 #pragma unroll
-        for (int i = 0; i < ITEMS; ++i) {
-            const uint32_t j = (uint32_t)(i * THREADS + tid_l);
-            const K x = s.keys[t][j];
-            const uint32_t dest = min(s.out_base[t][digit_of<CODE>(x, shift, mask)] + j, n32 - 1u);
-            keys_out[dest] = x;
-            if constexpr (PAIRS) vals_out[dest] = s.vals[t][j];
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t lo = lo_[k];
+                const uint32_t hi = lo + tt_[k] - ((uint32_t)(d0 + k) == mask ? pad : 0u);
+                const uint32_t base = lo - of_[k];         // output index of tile slot 0 of the digit
+                const uint32_t open = lo & ~(LINE - 1u);   // line holding the carry
+                const uint32_t next = hi & ~(LINE - 1u);   // line left open after this tile
+                // Carry lanes before the block's first index belong to the
+                // previous block.
+                const uint32_t mine = st_[k] > open ? st_[k] - open : 0u;
+                // The carry goes out when its line fills, or at the block's end
+                // (never past n: only a key array changed under a running sort
+                // could make the counts say otherwise).
+                const uint32_t put_to = (final_tile || next > open) ? min(lo, n32) - min(open, n32) : 0u;
+                // Lanes kept from the old carry (line still open) and loaded
+                // from the tile.
+                const uint32_t keep = next == open ? lo - open : 0u;
+                const uint32_t fill = final_tile ? 0u : hi - next;
+                s.place[d0 + k] = make_uint2(base, min(final_tile ? hi : next, n32));
+                if constexpr (CARRY_LDS)
+                    s.pend[d0 + k] = make_uint2(open, bit_range(mine, put_to));
+                else
+                    s.pend[d0 + k] = make_uint4(open, bit_range(mine, put_to), next - base, bit_range(keep, fill));
+                hi_[k] = hi;
+            }
+            reinterpret_cast<uint4 *>(s.run)[lane] = make_uint4(hi_[0], hi_[1], hi_[2], hi_[3]);
         }
-    };
-    // Region t holding the block's last tile, with `valid` keys.
-    auto store_last = [&](int t, int valid) {
+        __syncthreads();
+
+        // Stores: the carry lanes whose line fills, then the tile's keys up to
+        // the last full line of their digit (all of them in the final tile),
+        // then the new carry.  No barrier follows: LDS is next written after
+        // the next tile's rank barrier.
         int tid_l = tid;
         asm volatile("" : "+v"(tid_l));
+        const uint32_t e = (uint32_t)tid_l % LINE;
+        const uint32_t drow = (uint32_t)tid_l / LINE;
+        if constexpr (CARRY_LDS) {
+            // Consecutive threads take consecutive lanes of a digit's carry
+            // line: a wave stores whole lines.
 #pragma unroll
-        for (int i = 0; i < ITEMS; ++i) {
-            const int j = i * THREADS + tid_l;
-            if (j < valid) {
-                const K x = s.keys[t][j];
-                const uint32_t dest = s.out_base[t][digit_of<CODE>(x, shift, mask)] + (uint32_t)j;
-                if (dest < n32) {
-                    keys_out[dest] = x;
-                    if constexpr (PAIRS) vals_out[dest] = s.vals[t][j];
+            for (int i = 0; i < CARRY; ++i) {
+                const uint32_t d = (uint32_t)i * (THREADS / LINE) + drow;
+                const uint2 pe = s.pend[d];
+                store_out<WIDE>(s.carry[d][e], keys_out, kout_buf, pe.x + e, ((pe.y >> e) & 1u) != 0u);
+            }
+            // Every carry lane is read before the tile's held-back keys
+            // overwrite the lines that filled.
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < ITEMS; ++i) {
+                const uint32_t j = (uint32_t)(i * THREADS + tid_l);
+                const K x = s.keys[j];
+                const uint32_t d = digit_of<CODE>(x, shift, mask);
+                const uint2 pl = s.place[d];
+                const uint32_t pos = pl.x + j;
+                const bool put = pos < pl.y;
+                store_out<WIDE>(x, keys_out, kout_buf, pos, put);
+                // Past the last full line: the key joins the carry (in the
+                // final tile these are padding slots, and the carry is dead).
+                if (!put) s.carry[d][pos & (LINE - 1u)] = x;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < CARRY; ++i) {
+                const uint4 pe = s.pend[(uint32_t)i * (THREADS / LINE) + drow];
+                const bool put = ((pe.y >> e) & 1u) != 0u;
+                store_out<WIDE>(ck[i], keys_out, kout_buf, pe.x + e, put);
+                if constexpr (PAIRS) store_out<WIDE>(cv[i], vals_out, vout_buf, pe.x + e, put);
+            }
+#pragma unroll
+            for (int i = 0; i < ITEMS; ++i) {
+                const uint32_t j = (uint32_t)(i * THREADS + tid_l);
+                const K x = s.keys[j];
+                const uint2 pl = s.place[digit_of<CODE>(x, shift, mask)];
+                const uint32_t pos = pl.x + j;
+                const bool put = pos < pl.y;
+                store_out<WIDE>(x, keys_out, kout_buf, pos, put);
+                if constexpr (PAIRS) store_out<WIDE>(s.vals[j], vals_out, vout_buf, pos, put);
+            }
+            // Re-read the carry descriptors rather than keep them live across
+            // the stores (registers bound the workgroups per CU here).
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int i = 0; i < CARRY; ++i) {
+                const uint4 pe = s.pend[(uint32_t)i * (THREADS / LINE) + drow];
+                const bool take = ((pe.w >> e) & 1u) != 0u;
+                const uint32_t slot = (pe.z + e) & (uint32_t)(TILE - 1);
+                // Read unconditionally (the slot is always in the tile), so the
+                // reload is a select rather than a branch per carry register.
+                K x = s.keys[slot];
+                asm volatile("" : "+v"(x));
+                ck[i] = take ? x : ck[i];
+                if constexpr (PAIRS) {
+                    uint32_t y = s.vals[slot];
+                    asm volatile("" : "+v"(y));
+                    cv[i] = take ? y : cv[i];
                 }
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     };
 
-    // Tile t's keys are loaded two tiles ahead: the loads are issued as soon
-    // as tile t-2 has been moved to LDS, before tile t-2's stores.  The memory
-    // counter is in order, so waiting for those keys (at tile t) never waits
-    // for stores issued after them; stores drain while the next tiles rank.
-    // The first two tiles load B before A and wait for both, so that on entry
-    // to the loop neither buffer is in flight, and the loop has one exit and
-    // the same memory operations on every path: each wait below is counted
-    // exactly, not conservatively.  A wave keeps at most 63 memory operations
-    // in flight, so A's loads are issued only after B's keys have arrived:
-    // then no wait covers more than the stores.
+    // One tile ahead: tile t+1's loads are issued before tile t is ranked, so
+    // they are in flight during its rank and ahead of its stores; the memory
+    // counter is in order, so the wait for them (before tile t+1) never waits
+    // for those stores.  Buffers a and b alternate, unrolled by two so each
+    // stays in fixed registers, and a is ready at the loop head.
     K a[ITEMS], b[ITEMS];
-    prefetch(b, blk_begin + TILE);
     prefetch(a, blk_begin);
     ready(a);
-
-    // Tiles go in pairs, A in buffer a and B in buffer b.  The loop takes the
-    // pairs before the block's last tile; the last one or two tiles (the last
-    // may be short) follow it.
     const int tiles = (int)((blk_end - blk_begin + TILE - 1) / TILE);
     const int pairs = (tiles - 1) / 2;
     int64_t ta = blk_begin;
     for (int p = 0; p < pairs; ++p, ta += 2 * TILE) {
-        const int64_t tb = ta + TILE;
-        rank_tile(a, ta, 0, 0);
-        if constexpr (SUB == 1) {
-            __syncthreads();
-            store_full(0);
-        }
+        prefetch(b, ta + TILE);
+        process_tile(a, ta, 0, false);
         ready(b);
         prefetch(a, ta + 2 * TILE);
-        rank_tile(b, tb, SUB - 1, 1);
-        prefetch(b, tb + 2 * TILE);
-        __syncthreads();
-#pragma unroll
-        for (int t = 0; t < SUB; ++t) store_full(t);
+        process_tile(b, ta + TILE, 1, false);
         ready(a);
     }
-
-    rank_tile(a, ta, 0, 0);
     if (tiles - 2 * pairs == 1) {
-        __syncthreads();
-        store_last(0, (int)(blk_end - ta));
+        process_tile(a, ta, 0, true);
     } else {
-        if constexpr (SUB == 1) {
-            __syncthreads();
-            store_full(0);
-        }
+        prefetch(b, ta + TILE);
+        process_tile(a, ta, 0, false);
         ready(b);
-        rank_tile(b, ta + TILE, SUB - 1, 1);
-        __syncthreads();
-        if constexpr (SUB == 2) store_full(0);
-        store_last(SUB - 1, (int)(blk_end - ta - TILE));
+        process_tile(b, ta + TILE, 1, true);
     }
 }
 

@@ -58,14 +58,15 @@ constexpr int tiny_max()
                                                                        : 4096;
 }
 
-// Downsweep tile shapes (waves per workgroup x keys per lane): 8192-key
-// tiles.  The tile size sets how many keys of each digit a workgroup writes
-// in one piece (about tile/256 per tile): longer pieces leave fewer
-// partly-written 128-byte lines, which cost HBM bandwidth.
-constexpr int kWaves32 = 8, kItems32 = 16;
-constexpr int kWaves64 = 8, kItems64 = 16;
-
-int tile_keys(KeyKind kind) { return key_bytes(kind) == 8 ? kWaves64 * 64 * kItems64 : kWaves32 * 64 * kItems32; }
+// Downsweep tile shapes, 16 keys per lane throughout: 32-bit keys alone run
+// 16 waves (16,384-key tiles; the carry of the write-combining stores fits in
+// LDS beside the tile, one workgroup per CU), pairs and 64-bit keys run 8
+// waves (8,192-key tiles, one workgroup per CU, carry in registers).  Longer
+// tiles give each digit longer runs and spread the per-tile work (the digit
+// scan, the carry stores) over more keys.
+constexpr int kItems = 16;
+constexpr int waves_for(int kbytes, bool pairs) { return kbytes == 4 && !pairs ? 16 : 8; }
+int tile_keys(KeyKind kind, bool pairs) { return waves_for(key_bytes(kind), pairs) * 64 * kItems; }
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -209,7 +210,7 @@ Layout make_layout(const Request &rq)
     Layout L;
     const size_t ksz = (size_t)key_bytes(rq.kind);
     L.passes = (rq.end_bit - rq.begin_bit + kRadixBits - 1) / kRadixBits;
-    L.tile = tile_keys(rq.kind);
+    L.tile = tile_keys(rq.kind, rq.vals_in != nullptr);
     L.tiles = (rq.n + L.tile - 1) / L.tile;
     L.max_cols = (int)std::min<int64_t>(L.tiles * kMaxSplit, kMaxBlocks);
     L.kplan = make_plan(L.passes, rq.keys_in == rq.keys_out);
@@ -282,23 +283,19 @@ hipError_t launch_scan(uint32_t *counts, uint32_t *rowtot, int blocks, hipStream
     });
 }
 
-// Tiles written out together by the downsweep, per key type: two for 32-bit
-// keys (76 KB of LDS for keys only, two workgroups per CU); one for 64-bit
-// keys, whose tile alone takes 64 KB.
-template <typename K, bool PAIRS>
-constexpr int sub_tiles()
+// Outputs past 2 GiB take the downsweep with plain stores: the buffer stores'
+// byte offsets are 32-bit.
+template <typename K>
+bool wide_output(int64_t n)
 {
-#ifdef LRS_SUB
-    return LRS_SUB;
-#else
-    return sizeof(K) == 4 ? 2 : 1;
-#endif
+    return n * (int64_t)sizeof(K) > ((int64_t)1 << 31);
 }
 
 template <typename K, bool PAIRS, int WAVES, int ITEMS, int CODE>
-auto downsweep_fn()
+auto downsweep_fn(bool wide)
 {
-    return downsweep_kernel<K, PAIRS, WAVES, ITEMS, sub_tiles<K, PAIRS>(), CODE>;
+    return wide ? downsweep_kernel<K, PAIRS, WAVES, ITEMS, CODE, true>
+                : downsweep_kernel<K, PAIRS, WAVES, ITEMS, CODE, false>;
 }
 
 struct PassRoute {
@@ -314,7 +311,7 @@ hipError_t launch_downsweep(const SortBufs &bufs, uint32_t *route_k, uint32_t *r
                             int blocks, int cols, int split, int shift, uint32_t mask, hipStream_t stream)
 {
     return launch(LRS_KERNEL_DOWNSWEEP, stream, [&] {
-        downsweep_fn<K, PAIRS, WAVES, ITEMS, CODE>()<<<blocks, WAVES * 64, 0, stream>>>(
+        downsweep_fn<K, PAIRS, WAVES, ITEMS, CODE>(wide_output<K>(n))<<<blocks, WAVES * 64, 0, stream>>>(
             bufs, route_k, route_v, pr.pass, pr.ksrc_fixed, pr.vsrc_fixed, pr.kplanned, pr.vplanned, pr.last,
             counts, rowtot, n, block_len, cols, split, shift, mask);
     });
@@ -322,12 +319,13 @@ hipError_t launch_downsweep(const SortBufs &bufs, uint32_t *route_k, uint32_t *r
 
 // The kernel whose occupancy sets the number of blocks for this key type.
 template <typename K, bool PAIRS, int WAVES, int ITEMS, int CODE>
-hipError_t blocks_for(int64_t tiles, int *blocks)
+hipError_t blocks_for(int64_t n, int64_t tiles, int *blocks)
 {
     int cus = 0, per_cu = 0;
     hipError_t err = device_cus(&cus);
     if (err != hipSuccess) return err;
-    err = occupancy((const void *)downsweep_fn<K, PAIRS, WAVES, ITEMS, CODE>(), WAVES * 64, &per_cu);
+    err = occupancy((const void *)downsweep_fn<K, PAIRS, WAVES, ITEMS, CODE>(wide_output<K>(n)), WAVES * 64,
+                    &per_cu);
     if (err != hipSuccess) return err;
     // The downsweep reads a block's keys through a buffer whose size field is
     // 32-bit: keep every block below 2^30 bytes (at least 32 blocks at the
@@ -360,7 +358,7 @@ lrs_status run_passes(const Request &rq, const Layout &L, char *temp, hipStream_
 {
     constexpr int TILE = WAVES * 64 * ITEMS;
     int want_blocks = 0;
-    if (blocks_for<K, PAIRS, WAVES, ITEMS, CODE>(L.tiles, &want_blocks) != hipSuccess) return LRS_ERR_HIP;
+    if (blocks_for<K, PAIRS, WAVES, ITEMS, CODE>(rq.n, L.tiles, &want_blocks) != hipSuccess) return LRS_ERR_HIP;
     const int64_t tiles_per_block = (L.tiles + want_blocks - 1) / want_blocks;
     const int64_t block_len = tiles_per_block * TILE;
     const int blocks = (int)((rq.n + block_len - 1) / block_len);
@@ -433,10 +431,8 @@ lrs_status run_kind(bool pairs, const Request &r, const Layout &L, char *temp, h
 {
     if (pairs && r.n <= tiny_max<K, true>()) return run_tiny<K, true, CODE>(r, stream);
     if (!pairs && r.n <= tiny_max<K, false>()) return run_tiny<K, false, CODE>(r, stream);
-    constexpr int W = sizeof(K) == 8 ? kWaves64 : kWaves32;
-    constexpr int I = sizeof(K) == 8 ? kItems64 : kItems32;
-    if (pairs) return run_passes<K, true, W, I, CODE>(r, L, temp, stream);
-    return run_passes<K, false, W, I, CODE>(r, L, temp, stream);
+    if (pairs) return run_passes<K, true, waves_for(sizeof(K), true), kItems, CODE>(r, L, temp, stream);
+    return run_passes<K, false, waves_for(sizeof(K), false), kItems, CODE>(r, L, temp, stream);
 }
 
 lrs_status sort_entry(const Request &rq, void *d_temp, size_t *temp_bytes, hipStream_t stream)

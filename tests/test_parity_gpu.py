@@ -24,7 +24,12 @@ from sorting_lsd_radix_sort_amd import inputs
 
 pytestmark = pytest.mark.gpu
 
-TILE = 8192  # keys per downsweep tile
+TILE = 8192  # keys per downsweep tile (pairs and 64-bit keys; 32-bit keys alone: 2 * TILE)
+CUS = 256    # compute units of the part: one downsweep workgroup per CU
+
+
+def tile_of(key_bytes: int, pairs: bool) -> int:
+    return 2 * TILE if key_bytes == 4 and not pairs else TILE
 BIG_N = 1 << 17  # above every single-workgroup size limit: the multi-kernel path
 # largest n sorted by one workgroup in LDS, per (key bytes, pairs)
 TINY_MAX = {(4, False): 16384, (4, True): 8192, (8, False): 8192, (8, True): 4096}
@@ -108,6 +113,36 @@ def test_multi_tile_blocks_vs_oracle(key_type, n, pairs):
     bits = 8 * keys.dtype.itemsize
     announce("multi-tile %s n=%d pairs=%s" % (key_type, n, pairs))
     _compare(keys, vals, 0, bits)
+
+
+@pytest.mark.parametrize("key_type,pairs", [("u32", False), ("u32", True), ("f32", False), ("u64", False),
+                                            ("i64", True)])
+def test_block_shapes_vs_oracle(key_type, pairs):
+    """Sizes around whole tiles and whole blocks of tiles, with one and several
+    tiles per block, so that blocks end on full and short tiles, after an odd
+    and an even number of tiles."""
+    ksz = np.dtype(inputs.KEY_DTYPES[key_type]).itemsize
+    tile = tile_of(ksz, pairs)
+    bits = 8 * ksz
+    for k in (1, 2, 3):
+        for r in (-1, 0, 1, tile // 2 + 3):
+            n = CUS * k * tile + r
+            keys = inputs.random_keys(key_type, n, 40 + k, "uniform")
+            vals = np.arange(n, dtype=np.uint32) if pairs else None
+            announce("block shapes %s pairs=%s n=%d" % (key_type, pairs, n))
+            _compare(keys, vals, 0, bits)
+
+
+@pytest.mark.parametrize("key_type,n", [("u32", (1 << 29) + 12_345), ("u64", (1 << 28) + 3)])
+def test_outputs_past_2gib(key_type, n):
+    """Outputs larger than a 32-bit byte offset reaches take the downsweep's
+    plain-store form; checked by the properties that pin the stable sort."""
+    keys = inputs.random_keys(key_type, n, 11, "dup" if key_type == "u32" else "uniform")
+    vals = np.arange(n, dtype=np.uint32)
+    bits = 8 * keys.dtype.itemsize
+    announce("wide output %s n=%d" % (key_type, n))
+    got_k, got_v = gpu_sort(keys, vals, 0, bits)
+    checks.check_pairs(keys, got_k, got_v, 0, bits)
 
 
 # ------------------------------------------------------------------ in-place use
