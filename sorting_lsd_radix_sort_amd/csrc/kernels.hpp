@@ -481,11 +481,20 @@ constexpr bool carry_in_lds()
 }
 
 // Waves per SIMD the register allocation has to allow: 32-bit keys alone run
-// 16 waves per CU (LDS allows it); the other shapes run 8.
+// 16 waves per CU (one 16-wave or two 8-wave workgroups); the other shapes 8.
 template <typename K, bool PAIRS>
 constexpr int downsweep_waves_per_simd()
 {
     return carry_in_lds<K, PAIRS>() ? 4 : 2;
+}
+
+// Whether half of the rank's matching goes through the LDS table: everywhere
+// except 8-wave workgroups of 32-bit keys alone, where the table's 16 KB would
+// cost the second workgroup per CU.
+template <typename K, bool PAIRS, int WAVES>
+constexpr bool match_in_lds()
+{
+    return !(carry_in_lds<K, PAIRS>() && WAVES == 8);
 }
 
 template <typename K, bool PAIRS, int WAVES, int ITEMS>
@@ -505,7 +514,8 @@ struct DownsweepSmem {
     // current tile counts in one; in the other, each wave's own row holds its
     // slot bases (tile slot of its first key of digit d) for the scatter.
     alignas(16) uint16_t wave_count[2][WAVES][kRadix];
-    alignas(16) unsigned long long match_table[WAVES][kRadix];  // per-wave slots of match_digit_lds
+    static constexpr bool kMatchLds = match_in_lds<K, PAIRS, WAVES>();
+    alignas(16) unsigned long long match_table[kMatchLds ? WAVES : 1][kMatchLds ? kRadix : 1];  // match_digit_lds slots
     // Per digit d: {output index of tile slot 0 of d, end of the indices
     // stored from the tile}.
     alignas(16) uint2 place[kRadix];
@@ -670,8 +680,8 @@ __global__ __launch_bounds__(WAVES *kWave)
             uint16_t *counter = &count[wave][d];
             const uint32_t prior = *counter;
             uint32_t lo, hi;
-            if (i & 1)
-                match_digit_lds(&s.match_table[wave][d], lane_bit, lo, hi);
+            if ((i & 1) && Smem::kMatchLds)
+                match_digit_lds(&s.match_table[Smem::kMatchLds ? wave : 0][Smem::kMatchLds ? d : 0], lane_bit, lo, hi);
             else
                 match_digit(d, lo, hi);
             *counter = (uint16_t)(prior + __popc(lo) + __popc(hi));

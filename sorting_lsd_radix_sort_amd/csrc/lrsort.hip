@@ -58,15 +58,17 @@ constexpr int tiny_max()
                                                                        : 4096;
 }
 
-// Downsweep tile shapes, 16 keys per lane throughout: 32-bit keys alone run
+// Downsweep tile shapes, 16 keys per lane throughout.  32-bit keys alone run
 // 16 waves (16,384-key tiles; the carry of the write-combining stores fits in
-// LDS beside the tile, one workgroup per CU), pairs and 64-bit keys run 8
-// waves (8,192-key tiles, one workgroup per CU, carry in registers).  Longer
-// tiles give each digit longer runs and spread the per-tile work (the digit
-// scan, the carry stores) over more keys.
+// LDS beside the tile, one workgroup per CU) from 2^21 keys; longer tiles give
+// each digit longer runs and spread the per-tile work (the digit scan, the
+// carry stores) over more keys.  Below that (where the 8-wave shape measured
+// faster: more workgroups for the same n), and for pairs and 64-bit keys, 8
+// waves (8,192-key tiles).
 constexpr int kItems = 16;
-constexpr int waves_for(int kbytes, bool pairs) { return kbytes == 4 && !pairs ? 16 : 8; }
-int tile_keys(KeyKind kind, bool pairs) { return waves_for(key_bytes(kind), pairs) * 64 * kItems; }
+constexpr int64_t kWideTileMinKeys = (int64_t)1 << 21;
+constexpr bool wide_tiles(int kbytes, bool pairs, int64_t n) { return kbytes == 4 && !pairs && n >= kWideTileMinKeys; }
+int tile_keys(KeyKind kind, bool pairs, int64_t n) { return (wide_tiles(key_bytes(kind), pairs, n) ? 16 : 8) * 64 * kItems; }
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -210,7 +212,7 @@ Layout make_layout(const Request &rq)
     Layout L;
     const size_t ksz = (size_t)key_bytes(rq.kind);
     L.passes = (rq.end_bit - rq.begin_bit + kRadixBits - 1) / kRadixBits;
-    L.tile = tile_keys(rq.kind, rq.vals_in != nullptr);
+    L.tile = tile_keys(rq.kind, rq.vals_in != nullptr, rq.n);
     L.tiles = (rq.n + L.tile - 1) / L.tile;
     L.max_cols = (int)std::min<int64_t>(L.tiles * kMaxSplit, kMaxBlocks);
     L.kplan = make_plan(L.passes, rq.keys_in == rq.keys_out);
@@ -431,8 +433,11 @@ lrs_status run_kind(bool pairs, const Request &r, const Layout &L, char *temp, h
 {
     if (pairs && r.n <= tiny_max<K, true>()) return run_tiny<K, true, CODE>(r, stream);
     if (!pairs && r.n <= tiny_max<K, false>()) return run_tiny<K, false, CODE>(r, stream);
-    if (pairs) return run_passes<K, true, waves_for(sizeof(K), true), kItems, CODE>(r, L, temp, stream);
-    return run_passes<K, false, waves_for(sizeof(K), false), kItems, CODE>(r, L, temp, stream);
+    if (pairs) return run_passes<K, true, 8, kItems, CODE>(r, L, temp, stream);
+    if constexpr (sizeof(K) == 4) {
+        if (wide_tiles(4, false, r.n)) return run_passes<K, false, 16, kItems, CODE>(r, L, temp, stream);
+    }
+    return run_passes<K, false, 8, kItems, CODE>(r, L, temp, stream);
 }
 
 lrs_status sort_entry(const Request &rq, void *d_temp, size_t *temp_bytes, hipStream_t stream)

@@ -133,6 +133,16 @@ def test_block_shapes_vs_oracle(key_type, pairs):
             _compare(keys, vals, 0, bits)
 
 
+@pytest.mark.parametrize("key_type", ["u32", "i32", "f32"])
+def test_tile_shape_switch_vs_oracle(key_type):
+    """32-bit keys alone switch from 8,192- to 16,384-key tiles at 2^21 keys."""
+    for n in ((1 << 21) - 1, 1 << 21, (1 << 21) + 1):
+        keys = inputs.random_keys(key_type, n, 60, "fmix" if key_type == "f32" else "uniform")
+        announce("tile shape switch %s n=%d" % (key_type, n))
+        _compare(keys, None, 0, 32)
+        _compare(keys, None, 3, 29)
+
+
 @pytest.mark.parametrize("key_type,n", [("u32", (1 << 29) + 12_345), ("u64", (1 << 28) + 3)])
 def test_outputs_past_2gib(key_type, n):
     """Outputs larger than a 32-bit byte offset reaches take the downsweep's
