@@ -549,7 +549,7 @@ __global__ __launch_bounds__(WAVES *kWave)
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform: per-wave choices are scalar
     const int blk = blockIdx.x;
     const int64_t blk_begin = (int64_t)blk * block_len;
     const int64_t blk_end = blk_begin + block_len < n ? blk_begin + block_len : n;
@@ -590,7 +590,7 @@ __global__ __launch_bounds__(WAVES *kWave)
     uint32_t *__restrict__ vals_out = PAIRS ? (uint32_t *)bufs.vals[vdst] : nullptr;
 
     // The block's first output index of each digit (digit start plus the
-    // block's prefix); wave 0 alone reads and advances these.
+    // block's prefix); waves 0-3 read and advance these, each its own digits.
     if (wave == 0) {
         const uint4 start = wave_scan_digits(tot4);
         const uint4 first =
@@ -695,15 +695,20 @@ __global__ __launch_bounds__(WAVES *kWave)
         // own prefix over the waves before it, and the tile's exclusive prefix
         // over digits.  Redundant across waves, but it needs no second barrier
         // and no wave waits for another.
-        uint4 tot = make_uint4(0u, 0u, 0u, 0u), off;
+        uint4 tot, off;
         {
-            uint4 before = make_uint4(0u, 0u, 0u, 0u);
+            // Two 16-bit counts per word: a tile's total per digit is below
+            // 2^16, so the packed sums never carry into each other.
+            uint2 sum = make_uint2(0u, 0u), pre = make_uint2(0u, 0u);
 #pragma unroll
             for (int w = 0; w < WAVES; ++w) {
                 const uint2 c = reinterpret_cast<const uint2 *>(count[w])[lane];
-                if (w == wave) before = tot;
-                tot.x += c.x & 0xFFFFu; tot.y += c.x >> 16; tot.z += c.y & 0xFFFFu; tot.w += c.y >> 16;
+                if (w == wave) pre = sum;
+                sum.x += c.x;
+                sum.y += c.y;
             }
+            tot = make_uint4(sum.x & 0xFFFFu, sum.x >> 16, sum.y & 0xFFFFu, sum.y >> 16);
+            const uint4 before = make_uint4(pre.x & 0xFFFFu, pre.x >> 16, pre.y & 0xFFFFu, pre.y >> 16);
             off = wave_scan_digits(tot);
             reinterpret_cast<uint2 *>(slot_base[wave])[lane] =
                 make_uint2((before.x + off.x) | ((before.y + off.y) << 16),
@@ -719,46 +724,39 @@ __global__ __launch_bounds__(WAVES *kWave)
             if constexpr (PAIRS) s.vals[r[i]] = v[i];
         }
 
-        // Wave 0 places this tile's runs and plans its stores.
-        if (wave == 0) {
+        // Waves 0-3 place this tile's runs and plan its stores, wave k taking
+        // digit 4*lane + k (the offsets are in every wave, 4 digits per lane).
+        if (wave < 4) {
+            const int k = wave;
+            const uint32_t d = 4u * (uint32_t)lane + (uint32_t)k;
+            const uint32_t tt = k == 0 ? tot.x : k == 1 ? tot.y : k == 2 ? tot.z : tot.w;
+            const uint32_t of = k == 0 ? off.x : k == 1 ? off.y : k == 2 ? off.z : off.w;
             // The padding slots of a short last tile were counted under digit
             // `mask`; they sit after that digit's real keys and are never
             // stored.
-            const uint32_t pad = (uint32_t)(TILE - valid);
-            const int d0 = 4 * lane;
-            const uint4 run4 = reinterpret_cast<const uint4 *>(s.run)[lane];
-            const uint4 start4 = reinterpret_cast<const uint4 *>(s.start)[lane];
-            const uint32_t lo_[4] = {run4.x, run4.y, run4.z, run4.w};
-            const uint32_t st_[4] = {start4.x, start4.y, start4.z, start4.w};
-            const uint32_t tt_[4] = {tot.x, tot.y, tot.z, tot.w};
-            const uint32_t of_[4] = {off.x, off.y, off.z, off.w};
-            uint32_t hi_[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint32_t lo = lo_[k];
-                const uint32_t hi = lo + tt_[k] - ((uint32_t)(d0 + k) == mask ? pad : 0u);
-                const uint32_t base = lo - of_[k];         // output index of tile slot 0 of the digit
-                const uint32_t open = lo & ~(LINE - 1u);   // line holding the carry
-                const uint32_t next = hi & ~(LINE - 1u);   // line left open after this tile
-                // Carry lanes before the block's first index belong to the
-                // previous block.
-                const uint32_t mine = st_[k] > open ? st_[k] - open : 0u;
-                // The carry goes out when its line fills, or at the block's end
-                // (never past n: only a key array changed under a running sort
-                // could make the counts say otherwise).
-                const uint32_t put_to = (final_tile || next > open) ? min(lo, n32) - min(open, n32) : 0u;
-                // Lanes kept from the old carry (line still open) and loaded
-                // from the tile.
-                const uint32_t keep = next == open ? lo - open : 0u;
-                const uint32_t fill = final_tile ? 0u : hi - next;
-                s.place[d0 + k] = make_uint2(base, min(final_tile ? hi : next, n32));
-                if constexpr (CARRY_LDS)
-                    s.pend[d0 + k] = make_uint2(open, bit_range(mine, put_to));
-                else
-                    s.pend[d0 + k] = make_uint4(open, bit_range(mine, put_to), next - base, bit_range(keep, fill));
-                hi_[k] = hi;
-            }
-            reinterpret_cast<uint4 *>(s.run)[lane] = make_uint4(hi_[0], hi_[1], hi_[2], hi_[3]);
+            const uint32_t lo = s.run[d];
+            const uint32_t hi = lo + tt - (d == mask ? (uint32_t)(TILE - valid) : 0u);
+            const uint32_t base = lo - of;               // output index of tile slot 0 of the digit
+            const uint32_t open = lo & ~(LINE - 1u);     // line holding the carry
+            const uint32_t next = hi & ~(LINE - 1u);     // line left open after this tile
+            // Carry lanes before the block's first index belong to the
+            // previous block.
+            const uint32_t first_idx = s.start[d];
+            const uint32_t mine = first_idx > open ? first_idx - open : 0u;
+            // The carry goes out when its line fills, or at the block's end
+            // (never past n: only a key array changed under a running sort
+            // could make the counts say otherwise).
+            const uint32_t put_to = (final_tile || next > open) ? min(lo, n32) - min(open, n32) : 0u;
+            // Lanes kept from the old carry (line still open) and loaded from
+            // the tile.
+            const uint32_t keep = next == open ? lo - open : 0u;
+            const uint32_t fill = final_tile ? 0u : hi - next;
+            s.place[d] = make_uint2(base, min(final_tile ? hi : next, n32));
+            if constexpr (CARRY_LDS)
+                s.pend[d] = make_uint2(open, bit_range(mine, put_to));
+            else
+                s.pend[d] = make_uint4(open, bit_range(mine, put_to), next - base, bit_range(keep, fill));
+            s.run[d] = hi;
         }
         __syncthreads();
 
@@ -773,28 +771,46 @@ __global__ __launch_bounds__(WAVES *kWave)
         if constexpr (CARRY_LDS) {
             // Consecutive threads take consecutive lanes of a digit's carry
             // line: a wave stores whole lines.
+            // Reads first, then stores (as for the tile's keys below).
+            uint2 pe[CARRY];
+            K cx[CARRY];
 #pragma unroll
             for (int i = 0; i < CARRY; ++i) {
                 const uint32_t d = (uint32_t)i * (THREADS / LINE) + drow;
-                const uint2 pe = s.pend[d];
-                store_out<WIDE>(s.carry[d][e], keys_out, kout_buf, pe.x + e, ((pe.y >> e) & 1u) != 0u);
+                pe[i] = s.pend[d];
+                cx[i] = s.carry[d][e];
             }
+#pragma unroll
+            for (int i = 0; i < CARRY; ++i)
+                store_out<WIDE>(cx[i], keys_out, kout_buf, pe[i].x + e, ((pe[i].y >> e) & 1u) != 0u);
             // Every carry lane is read before the tile's held-back keys
             // overwrite the lines that filled.
             __syncthreads();
+            // In phases, so that the LDS reads of all items are in flight
+            // together rather than one item's at a time: the keys, then their
+            // digits' placements, then the stores; then the keys past each
+            // digit's last full line join the carry (in the final tile these
+            // are padding slots, and the carry is dead).  Only those lanes
+            // write (all lanes writing, the others to a spare row, measured
+            // slower).
+            K xk[ITEMS];
+            uint32_t pos[ITEMS];
+            uint32_t held = 0u;
+            uint2 pl[ITEMS];
+#pragma unroll
+            for (int i = 0; i < ITEMS; ++i) xk[i] = s.keys[i * THREADS + tid_l];
+#pragma unroll
+            for (int i = 0; i < ITEMS; ++i) pl[i] = s.place[digit_of<CODE>(xk[i], shift, mask)];
 #pragma unroll
             for (int i = 0; i < ITEMS; ++i) {
-                const uint32_t j = (uint32_t)(i * THREADS + tid_l);
-                const K x = s.keys[j];
-                const uint32_t d = digit_of<CODE>(x, shift, mask);
-                const uint2 pl = s.place[d];
-                const uint32_t pos = pl.x + j;
-                const bool put = pos < pl.y;
-                store_out<WIDE>(x, keys_out, kout_buf, pos, put);
-                // Past the last full line: the key joins the carry (in the
-                // final tile these are padding slots, and the carry is dead).
-                if (!put) s.carry[d][pos & (LINE - 1u)] = x;
+                pos[i] = pl[i].x + (uint32_t)(i * THREADS + tid_l);
+                held |= pos[i] < pl[i].y ? 0u : 1u << i;
             }
+#pragma unroll
+            for (int i = 0; i < ITEMS; ++i) store_out<WIDE>(xk[i], keys_out, kout_buf, pos[i], ((held >> i) & 1u) == 0u);
+#pragma unroll
+            for (int i = 0; i < ITEMS; ++i)
+                if ((held >> i) & 1u) s.carry[digit_of<CODE>(xk[i], shift, mask)][pos[i] & (LINE - 1u)] = xk[i];
         } else {
 #pragma unroll
             for (int i = 0; i < CARRY; ++i) {
