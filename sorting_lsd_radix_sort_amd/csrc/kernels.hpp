@@ -459,16 +459,17 @@ __device__ __forceinline__ uint32_t bit_range(uint32_t a, uint32_t b)
 
 // The lanes of the wave whose digit equals this lane's, through LDS: every
 // lane clears its digit's 64-bit slot of the wave's table, sets its own bit
-// there (an atomic OR, so the order of lanes does not matter) and reads the
-// slot back.  DS operations of one wave complete in issue order, so the read
-// sees every lane's bit.  Three LDS operations instead of the ballot form's 32
-// VALU instructions; the rank loop alternates the two forms so that neither
-// the VALU nor the LDS pipe carries all of the matching.
-__device__ __forceinline__ void match_digit_lds(unsigned long long *slot, unsigned long long lane_bit,
-                                                uint32_t &lo, uint32_t &hi)
+// there (an atomic OR on the slot's half that holds its bit, so the order of
+// lanes does not matter) and reads the slot back.  DS operations of one wave
+// complete in issue order, so the read sees every lane's bit.  Three LDS
+// operations instead of the ballot form's 32 VALU instructions; the rank loop
+// alternates the two forms so that neither the VALU nor the LDS pipe carries
+// all of the matching.
+__device__ __forceinline__ void match_digit_lds(unsigned long long *slot, uint32_t lane, uint32_t &lo,
+                                                uint32_t &hi)
 {
     *slot = 0ull;
-    atomicOr(slot, lane_bit);
+    atomicOr(reinterpret_cast<uint32_t *>(slot) + (lane >> 5), 1u << (lane & 31u));
     const unsigned long long m = *slot;
     lo = (uint32_t)m;
     hi = (uint32_t)(m >> 32);
@@ -651,7 +652,6 @@ __global__ __launch_bounds__(WAVES *kWave)
         const int valid = blk_end - tile_begin < TILE ? (int)(blk_end - tile_begin) : TILE;
         const bool full = valid == TILE;
         const int first = lane_first();
-        const unsigned long long lane_bit = 1ull << lane;
         uint32_t v[ITEMS];
         if constexpr (PAIRS) issue_tile_loads<uint32_t, ITEMS>(v, vals_buf, (uint32_t)(tile_begin - blk_begin), first);
         finish_tile<K, CODE, ITEMS>(kb, first, valid, full);
@@ -681,7 +681,8 @@ __global__ __launch_bounds__(WAVES *kWave)
             const uint32_t prior = *counter;
             uint32_t lo, hi;
             if ((i & 1) && Smem::kMatchLds)
-                match_digit_lds(&s.match_table[Smem::kMatchLds ? wave : 0][Smem::kMatchLds ? d : 0], lane_bit, lo, hi);
+                match_digit_lds(&s.match_table[Smem::kMatchLds ? wave : 0][Smem::kMatchLds ? d : 0], (uint32_t)lane,
+                                lo, hi);
             else
                 match_digit(d, lo, hi);
             *counter = (uint16_t)(prior + __popc(lo) + __popc(hi));
