@@ -39,6 +39,7 @@
 namespace lrs {
 
 constexpr int kRadixBits = 8;
+constexpr int kXcds = 8;  // accelerator complex dies of the part; used only to place work
 constexpr int kRadix = 1 << kRadixBits;
 constexpr int kWave = 64;
 
@@ -276,6 +277,16 @@ __global__ __launch_bounds__(THREADS) void upsweep_kernel(
     SortBufs bufs, const uint32_t *__restrict__ route, int pass, int src_fixed, uint32_t *__restrict__ counts,
     int64_t n, int64_t block_len, int num_blocks, int shift, uint32_t mask)
 {
+    // The count matrix is digit-major, so a workgroup's 256 counts land in 256
+    // different rows, 4 bytes in each 128-byte line.  Workgroups go to the
+    // chip's XCDs in turn (workgroup i to XCD i mod kXcds); column c is counted
+    // by workgroup (c mod per) * kXcds + c / per, so that each XCD counts a
+    // contiguous range of columns and a line's 32 counts are merged in one L2
+    // instead of reaching memory as partial writes from several.  (Any mapping
+    // is correct; this one only places the writes.)
+    const int per = (num_blocks + kXcds - 1) / kXcds;
+    const int col = (int)(blockIdx.x % kXcds) * per + (int)(blockIdx.x / kXcds);
+    if (col >= num_blocks) return;  // the launch rounds the grid up to kXcds * per
     const K *__restrict__ keys = (const K *)bufs.keys[pass_source(route, pass, src_fixed)];
     constexpr int WAVES = THREADS / kWave;
     // COPIES sub-histograms per wave (lane % COPIES picks one), padded by one
@@ -289,7 +300,7 @@ __global__ __launch_bounds__(THREADS) void upsweep_kernel(
     for (int i = tid; i < WAVES * COPIES * STRIDE; i += THREADS) (&hist[0][0])[i] = 0u;
     __syncthreads();
 
-    const int64_t begin = (int64_t)blockIdx.x * block_len;
+    const int64_t begin = (int64_t)col * block_len;
     const int64_t end = begin + block_len < n ? begin + block_len : n;
 
     count_range<K, CODE, THREADS>(keys, begin, end, h, tid, shift, mask);
@@ -299,7 +310,7 @@ __global__ __launch_bounds__(THREADS) void upsweep_kernel(
         uint32_t s = 0;
 #pragma unroll
         for (int w = 0; w < WAVES * COPIES; ++w) s += hist[w][d];
-        counts[(int64_t)d * num_blocks + blockIdx.x] = s;
+        counts[(int64_t)d * num_blocks + col] = s;
     }
 }
 

@@ -273,7 +273,8 @@ hipError_t launch_upsweep(const SortBufs &bufs, const uint32_t *route, int pass,
                           int64_t n, int64_t block_len, int blocks, int shift, uint32_t mask, hipStream_t stream)
 {
     return launch(LRS_KERNEL_UPSWEEP, stream, [&] {
-        upsweep_kernel<K, CODE, kUpsweepThreads><<<blocks, kUpsweepThreads, 0, stream>>>(
+        const int grid = (blocks + kXcds - 1) / kXcds * kXcds;  // see upsweep_kernel's column mapping
+        upsweep_kernel<K, CODE, kUpsweepThreads><<<grid, kUpsweepThreads, 0, stream>>>(
             bufs, route, pass, src_fixed, counts, n, block_len, blocks, shift, mask);
     });
 }
