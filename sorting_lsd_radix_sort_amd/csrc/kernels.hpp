@@ -12,15 +12,16 @@
 //              prefixes and stores the row total;
 //   downsweep  each workgroup walks the tiles of its block in order: loads a
 //              tile with coalesced reads, ranks every key stably inside the
-//              tile with 64-lane ballots, reorders the tile through LDS so that
-//              each digit's keys are contiguous, and writes them to
+//              tile with 64-lane match masks, reorders the tile through LDS so
+//              that each digit's keys are contiguous, and writes them to
 //              digit_start[d] + block_prefix[d] + (keys of digit d in earlier
 //              tiles of the block) + rank.
 //
 // Counting per block of many tiles instead of per tile keeps the count matrix a
 // few MB at any n (so the scan is cheap), and lets a workgroup continue each
-// digit's output run from one tile to the next, so a partial cache line at a
-// run's end is completed by the same workgroup soon after.
+// digit's output run from one tile to the next: it holds back the keys of the
+// 128-byte line a run leaves open and writes that line whole once a later tile
+// fills it.
 //
 // Stability: within a tile, key i's rank among equal digits counts only keys
 // before it in input order (the page's section 3, last paragraphs: the stable
@@ -378,6 +379,7 @@ __global__ __launch_bounds__(THREADS) void scan_kernel(uint32_t *__restrict__ co
 // No store sits in a branch, every path issues the same memory operations, and
 // the wait for the next tile's loads is counted exactly.  WIDE outputs use
 // plain stores under a branch instead.
+
 // Buffer resource over `bytes` bytes from `base`: buffer loads through it at
 // byte offsets at or past `bytes` return zero without touching memory.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_over(const void *base, uint32_t bytes)
