@@ -24,7 +24,7 @@ from sorting_lsd_radix_sort_amd import inputs
 
 pytestmark = pytest.mark.gpu
 
-TILE = 8192  # keys per downsweep tile (pairs and 64-bit keys; 32-bit keys alone: 2 * TILE)
+TILE = 8192  # keys per downsweep tile above 2^17 keys (pairs and 64-bit keys; 32-bit keys alone from 2^21: 2 * TILE)
 CUS = 256    # compute units of the part: one downsweep workgroup per CU
 
 
@@ -141,6 +141,20 @@ def test_tile_shape_switch_vs_oracle(key_type):
         announce("tile shape switch %s n=%d" % (key_type, n))
         _compare(keys, None, 0, 32)
         _compare(keys, None, 3, 29)
+
+
+@pytest.mark.parametrize("key_type,pairs", [("u32", False), ("u32", True), ("f32", True), ("u64", False),
+                                            ("i64", True)])
+def test_small_tile_switch_vs_oracle(key_type, pairs):
+    """Up to 2^17 keys the passes use 2,048-key tiles; above, the large tiles."""
+    ksz = np.dtype(inputs.KEY_DTYPES[key_type]).itemsize
+    bits = 8 * ksz
+    for n in ((1 << 17) - 1, 1 << 17, (1 << 17) + 1, 2048 * 40 + 3):
+        keys = inputs.random_keys(key_type, n, 61, "uniform")
+        vals = np.arange(n, dtype=np.uint32) if pairs else None
+        announce("small tile switch %s pairs=%s n=%d" % (key_type, pairs, n))
+        _compare(keys, vals, 0, bits)
+        _compare(keys, vals, 5, bits - 3)
 
 
 @pytest.mark.parametrize("key_type,n", [("u32", (1 << 29) + 12_345), ("u64", (1 << 28) + 3)])
