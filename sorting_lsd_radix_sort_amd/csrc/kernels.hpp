@@ -556,6 +556,9 @@ __global__ __launch_bounds__(WAVES *kWave)
     constexpr uint32_t LINE = Smem::kLine;
     constexpr bool CARRY_LDS = Smem::kCarryLds;
     constexpr int CARRY = (int)(kRadix * LINE) / THREADS;  // carry positions per thread
+    // Units of place[]: byte offsets where the tile's stores use them directly
+    // (32-bit keys alone, outputs below 2 GiB), else element indices.
+    constexpr uint32_t PU = CARRY_LDS && !WIDE ? (uint32_t)sizeof(K) : 1u;
     static_assert(THREADS >= kRadix, "one thread per digit is assumed");
     static_assert(TILE < 65536 && (TILE & (TILE - 1)) == 0, "16-bit ranks, power-of-two tile");
     static_assert(THREADS % LINE == 0 && (kRadix * LINE) % THREADS == 0, "carry lanes map evenly");
@@ -698,8 +701,11 @@ __global__ __launch_bounds__(WAVES *kWave)
                                 lo, hi);
             else
                 match_digit(d, lo, hi);
-            *counter = (uint16_t)(prior + __popc(lo) + __popc(hi));
-            r[i] = prior + lanes_below(lo, hi);
+            // (the lane-count instructions add their accumulator operand for free)
+            uint32_t part = __popc(lo) + prior;
+            asm volatile("" : "+v"(part));  // keeps the two adds in the popcounts' accumulators
+            *counter = (uint16_t)(__popc(hi) + part);
+            r[i] = __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, prior));
             asm volatile("" : "+v"(r[i]));  // formed here, so d and the masks die here
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -765,7 +771,7 @@ __global__ __launch_bounds__(WAVES *kWave)
             // the tile.
             const uint32_t keep = next == open ? lo - open : 0u;
             const uint32_t fill = final_tile ? 0u : hi - next;
-            s.place[d] = make_uint2(base, min(final_tile ? hi : next, n32));
+            s.place[d] = make_uint2(base * PU, min(final_tile ? hi : next, n32) * PU);
             if constexpr (CARRY_LDS)
                 s.pend[d] = make_uint2(open, bit_range(mine, put_to));
             else
@@ -802,14 +808,12 @@ __global__ __launch_bounds__(WAVES *kWave)
             __syncthreads();
             // In phases, so that the LDS reads of all items are in flight
             // together rather than one item's at a time: the keys, then their
-            // digits' placements, then the stores; then the keys past each
-            // digit's last full line join the carry (in the final tile these
+            // digits' placements, then the stores.  Keys past their digit's
+            // last full line join the carry instead (in the final tile these
             // are padding slots, and the carry is dead).  Only those lanes
             // write (all lanes writing, the others to a spare row, measured
             // slower).
             K xk[ITEMS];
-            uint32_t pos[ITEMS];
-            uint32_t held = 0u;
             uint2 pl[ITEMS];
 #pragma unroll
             for (int i = 0; i < ITEMS; ++i) xk[i] = s.keys[i * THREADS + tid_l];
@@ -817,14 +821,20 @@ __global__ __launch_bounds__(WAVES *kWave)
             for (int i = 0; i < ITEMS; ++i) pl[i] = s.place[digit_of<CODE>(xk[i], shift, mask)];
 #pragma unroll
             for (int i = 0; i < ITEMS; ++i) {
-                pos[i] = pl[i].x + (uint32_t)(i * THREADS + tid_l);
-                held |= pos[i] < pl[i].y ? 0u : 1u << i;
+                const uint32_t at = pl[i].x + (uint32_t)(i * THREADS + tid_l) * PU;  // in place[] units
+                const bool put = at < pl[i].y;
+                if constexpr (WIDE) {
+                    store_out<true>(xk[i], keys_out, kout_buf, at, put);
+                    if (!put) s.carry[digit_of<CODE>(xk[i], shift, mask)][at & (LINE - 1u)] = xk[i];
+                } else {
+                    buffer_store<K>(xk[i], kout_buf, put ? at : kStoreNowhere);
+                    // byte offset of lane (at / PU) % LINE in the digit's carry row
+                    if (!put)
+                        *reinterpret_cast<K *>(reinterpret_cast<char *>(&s.carry[0][0]) +
+                                               ((digit_of<CODE>(xk[i], shift, mask) * LINE * PU) |
+                                                (at & (LINE * PU - 1u)))) = xk[i];
+                }
             }
-#pragma unroll
-            for (int i = 0; i < ITEMS; ++i) store_out<WIDE>(xk[i], keys_out, kout_buf, pos[i], ((held >> i) & 1u) == 0u);
-#pragma unroll
-            for (int i = 0; i < ITEMS; ++i)
-                if ((held >> i) & 1u) s.carry[digit_of<CODE>(xk[i], shift, mask)][pos[i] & (LINE - 1u)] = xk[i];
         } else {
 #pragma unroll
             for (int i = 0; i < CARRY; ++i) {
