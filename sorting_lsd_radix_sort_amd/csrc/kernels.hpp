@@ -519,11 +519,12 @@ struct DownsweepSmem {
     // Output line, in positions: 128 bytes of keys; with values, 128 bytes of
     // values (and 128 or 256 of keys).
     static constexpr uint32_t kLine = PAIRS ? 32u : 128u / (uint32_t)sizeof(K);
+    // The carry, when in LDS: lane e of digit d holds output index (open line
+    // of d) + e.  First, so that a lane's address is (d*kLine + e)*sizeof(K)
+    // with no base.
+    K carry[kCarryLds ? kRadix : 1][kCarryLds ? kLine : 1];
     K keys[kTile];                     // the tile in digit order
     uint32_t vals[PAIRS ? kTile : 1];  // payload in the same order
-    // The carry, when in LDS: lane e of digit d holds output index (open line
-    // of d) + e.
-    K carry[kCarryLds ? kRadix : 1][kCarryLds ? kLine : 1];
     // Per-wave 16-bit digit counters, two buffers alternating by tile: the
     // current tile counts in one; in the other, each wave's own row holds its
     // slot bases (tile slot of its first key of digit d) for the scatter.
@@ -559,6 +560,7 @@ __global__ __launch_bounds__(WAVES *kWave)
     // Units of place[]: byte offsets where the tile's stores use them directly
     // (32-bit keys alone, outputs below 2 GiB), else element indices.
     constexpr uint32_t PU = CARRY_LDS && !WIDE ? (uint32_t)sizeof(K) : 1u;
+    constexpr uint32_t SB = sizeof(K) == 4 ? 4u : 1u;  // slot bases in bytes (4-byte keys) or slots
     static_assert(THREADS >= kRadix, "one thread per digit is assumed");
     static_assert(TILE < 65536 && (TILE & (TILE - 1)) == 0, "16-bit ranks, power-of-two tile");
     static_assert(THREADS % LINE == 0 && (kRadix * LINE) % THREADS == 0, "carry lanes map evenly");
@@ -679,7 +681,10 @@ __global__ __launch_bounds__(WAVES *kWave)
         // previous one (finished before the previous barrier) and by this
         // wave itself, as slot bases, in the previous tile.
         uint16_t(&count)[WAVES][kRadix] = s.wave_count[par];
-        uint16_t(&slot_base)[WAVES][kRadix] = s.wave_count[par ^ 1];
+        // This wave's counter row and slot-base row, addressed from one base
+        // so that each item's address serves both.
+        uint16_t *const row0 = &s.wave_count[0][wave][0];
+        constexpr int kBufStride = WAVES * kRadix;
         reinterpret_cast<uint2 *>(count[wave])[lane] = make_uint2(0u, 0u);
 
         // Rank within the wave: keys of earlier items (all lanes), then keys of
@@ -693,7 +698,7 @@ __global__ __launch_bounds__(WAVES *kWave)
 #pragma unroll
         for (int i = 0; i < ITEMS; ++i) {
             const uint32_t d = digit_of<CODE>(kb[i], shift, mask);
-            uint16_t *counter = &count[wave][d];
+            uint16_t *counter = row0 + (par * kBufStride + (int)d);
             const uint32_t prior = *counter;
             uint32_t lo, hi;
             if ((i & 1) && Smem::kMatchLds)
@@ -730,18 +735,26 @@ __global__ __launch_bounds__(WAVES *kWave)
             tot = make_uint4(sum.x & 0xFFFFu, sum.x >> 16, sum.y & 0xFFFFu, sum.y >> 16);
             const uint4 before = make_uint4(pre.x & 0xFFFFu, pre.x >> 16, pre.y & 0xFFFFu, pre.y >> 16);
             off = wave_scan_digits(tot);
-            reinterpret_cast<uint2 *>(slot_base[wave])[lane] =
-                make_uint2((before.x + off.x) | ((before.y + off.y) << 16),
-                           (before.z + off.z) | ((before.w + off.w) << 16));
+            // As byte offsets for 4-byte keys (below 2^16: a tile holds at
+            // most 2^14 keys), so the scatter address is one shift-add.
+            reinterpret_cast<uint2 *>(row0 + (par ^ 1) * kBufStride)[lane] =
+                make_uint2(((before.x + off.x) * SB & 0xFFFFu) | ((before.y + off.y) * SB << 16),
+                           ((before.z + off.z) * SB & 0xFFFFu) | ((before.w + off.w) * SB << 16));
         }
 
         // Reorder the tile in LDS: slot = tile offset of the digit + rank.
 #pragma unroll
-        for (int i = 0; i < ITEMS; ++i) r[i] += slot_base[wave][digit_of<CODE>(kb[i], shift, mask)];
+        for (int i = 0; i < ITEMS; ++i)
+            r[i] = r[i] * SB + row0[(par ^ 1) * kBufStride + (int)digit_of<CODE>(kb[i], shift, mask)];
 #pragma unroll
         for (int i = 0; i < ITEMS; ++i) {
-            s.keys[r[i]] = kb[i];
-            if constexpr (PAIRS) s.vals[r[i]] = v[i];
+            if constexpr (SB == 1) {
+                s.keys[r[i]] = kb[i];
+                if constexpr (PAIRS) s.vals[r[i]] = v[i];
+            } else {
+                *reinterpret_cast<K *>(reinterpret_cast<char *>(s.keys) + r[i]) = kb[i];
+                if constexpr (PAIRS) *reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(s.vals) + r[i]) = v[i];
+            }
         }
 
         // Waves 0-3 place this tile's runs and plan its stores, wave k taking
@@ -822,14 +835,15 @@ __global__ __launch_bounds__(WAVES *kWave)
 #pragma unroll
             for (int i = 0; i < ITEMS; ++i) {
                 const uint32_t at = pl[i].x + (uint32_t)(i * THREADS + tid_l) * PU;  // in place[] units
-                const bool put = at < pl[i].y;
+                const bool held = at >= pl[i].y;
                 if constexpr (WIDE) {
-                    store_out<true>(xk[i], keys_out, kout_buf, at, put);
-                    if (!put) s.carry[digit_of<CODE>(xk[i], shift, mask)][at & (LINE - 1u)] = xk[i];
+                    store_out<true>(xk[i], keys_out, kout_buf, at, !held);
+                    if (held) s.carry[digit_of<CODE>(xk[i], shift, mask)][at & (LINE - 1u)] = xk[i];
                 } else {
-                    buffer_store<K>(xk[i], kout_buf, put ? at : kStoreNowhere);
                     // byte offset of lane (at / PU) % LINE in the digit's carry row
-                    if (!put)
+                    if (!held)
+                        buffer_store<K>(xk[i], kout_buf, at);
+                    else
                         *reinterpret_cast<K *>(reinterpret_cast<char *>(&s.carry[0][0]) +
                                                ((digit_of<CODE>(xk[i], shift, mask) * LINE * PU) |
                                                 (at & (LINE * PU - 1u)))) = xk[i];
