@@ -4,7 +4,8 @@
 One step = one whole sort call (every pass: upsweep, scan, downsweep) of the
 workload's input, already resident in HBM, into a preallocated output with
 preallocated temp storage.  Default workload: 1e8 uint32 keys drawn uniformly
-from [0, 2^32) with seed 1, keys only, bits [0, 32), 4 passes of 8-bit digits.
+from [0, 2^32) with seed 1, keys only, bits [0, 32), 4 passes of 8-bit digits
+(--digit-bits 11: the same sort in 3 passes of 11-bit digits).
 
 Prints one JSON line with the throughput (Gkeys/s), the dominant kernel's
 roofline figures (from HIP events around each launch, on the launch stream)
@@ -82,6 +83,8 @@ def main() -> int:
                     help="keys of the input the CPU oracle sorts for the baseline")
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--digit-bits", type=int, default=8, choices=(8, 11),
+                    help="digit width of the passes (11: lrs_sort_digits with 2048-digit passes)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -104,14 +107,20 @@ def main() -> int:
     n = keys_np.size
     ksz = keys_np.dtype.itemsize
     vsz = 4 if vals_np is not None else 0
-    passes = (cfg.end_bit - cfg.begin_bit + 7) // 8
+    db = args.digit_bits
+    passes = (cfg.end_bit - cfg.begin_bit + db - 1) // db
 
     kin = torch.from_numpy(keys_np).to(dev)
     kout = torch.empty_like(kin)
     vin = torch.from_numpy(vals_np).to(dev) if vals_np is not None else None
     vout = torch.empty_like(vin) if vin is not None else None
     sfx = cfg.key_type
-    if vin is None:
+    if db != 8:
+        def fn(d_temp, temp_bytes, *rest):
+            ki, vi, ko, vo = rest[0], rest[1], rest[2], rest[3]
+            return lrs.lrs_sort_digits(sfx, db, d_temp, temp_bytes, ki, vi, ko, vo, *rest[4:])
+        arrays = (kin, vin, kout, vout)
+    elif vin is None:
         fn = getattr(lrs, "lrs_sort_keys_" + sfx)
         arrays = (kin, kout)
     else:
@@ -204,7 +213,7 @@ def main() -> int:
     copy_gbs = 2 * n * ksz / (copy_ms * 1e-3) / 1e9
 
     workload = cfg.name
-    traffic = measured_traffic(workload)
+    traffic = measured_traffic(workload) if db == 8 else None
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -237,6 +246,7 @@ def main() -> int:
         "config": {"workload": cfg.name, "description": cfg.description, "n": n,
                    "key": cfg.key_type, "values": "u32" if vals_np is not None else None,
                    "begin_bit": cfg.begin_bit, "end_bit": cfg.end_bit, "passes": passes,
+                   "digit_bits": db,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "downsweep", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,

@@ -122,6 +122,40 @@ lrs_status lrs_sort_pairs_f64(void *d_temp, size_t *temp_bytes,
                               double *d_keys_out, uint32_t *d_values_out,
                               int64_t n, int begin_bit, int end_bit, hipStream_t stream);
 
+/* Key types of lrs_sort_digits, with the order codes of the typed calls. */
+typedef enum lrs_key_type {
+    LRS_KEY_U32 = 0,
+    LRS_KEY_I32 = 1,
+    LRS_KEY_F32 = 2,
+    LRS_KEY_U64 = 3,
+    LRS_KEY_I64 = 4,
+    LRS_KEY_F64 = 5
+} lrs_key_type;
+
+/* The sort of the typed calls above, for any key type, with the digit width
+ * chosen: digit_bits 8 is what the typed calls run; digit_bits 11 sorts by
+ * 11-bit digits, 2048 buckets per pass, so ceil((end_bit - begin_bit) / 11)
+ * passes (3 instead of 4 for 32-bit keys, the last digit taking what bits are
+ * left), as the kwkr.cn essay on bitonic vs. LSD radix sort suggests in
+ * sections 3.4 and 5.2 and the page "GPU radix sort ..." weighs in section 4
+ * (fewer passes against larger histograms and scans).  The result is the same
+ * for either width: a stable sort is determined by the keys' order.
+ *  - key_type: an lrs_key_type; d_keys_in / d_keys_out point to arrays of that
+ *    type.
+ *  - d_values_in and d_values_out: both NULL for a keys-only sort, else both
+ *    uint32 arrays of n values that move with the keys (pair sort).  One NULL
+ *    and the other not, with n > 0, gives LRS_ERR_INVALID_ARG.
+ *  - digit_bits other than 8 or 11 gives LRS_ERR_INVALID_ARG.
+ *  - Sorts small enough for the library's one-workgroup path (some thousands
+ *    of keys) take that path for either width.
+ * Temp storage, streams, in-place use, bit range, n and alignment follow the
+ * conventions at the top of this file; the temp query must pass the same
+ * digit_bits (11-bit sorts need a count matrix 8 times larger, up to 32 MB). */
+lrs_status lrs_sort_digits(lrs_key_type key_type, int digit_bits, void *d_temp, size_t *temp_bytes,
+                           const void *d_keys_in, const uint32_t *d_values_in, void *d_keys_out,
+                           uint32_t *d_values_out, int64_t n, int begin_bit, int end_bit,
+                           hipStream_t stream);
+
 /* Static description of a status code (never NULL). */
 const char *lrs_status_string(lrs_status status);
 

@@ -27,7 +27,10 @@ KERNEL_NAMES = {0: "upsweep", 1: "scan", 2: "downsweep", 3: "copy", 4: "finalize
 
 KEY_TYPES = ("u32", "i32", "f32", "u64", "i64", "f64")
 SORT_FUNCTIONS = tuple("lrs_sort_keys_" + t for t in KEY_TYPES) + tuple("lrs_sort_pairs_" + t for t in KEY_TYPES)
-EXPORTED = SORT_FUNCTIONS + ("lrs_status_string", "lrs_device_copy", "lrs_prof_start",
+# lrs_key_type codes of lrs_sort_digits
+KEY_TYPE_CODES = {"u32": 0, "i32": 1, "f32": 2, "u64": 3, "i64": 4, "f64": 5}
+DIGIT_BITS = (8, 11)
+EXPORTED = SORT_FUNCTIONS + ("lrs_sort_digits", "lrs_status_string", "lrs_device_copy", "lrs_prof_start",
                              "lrs_prof_stop", "lrs_prof_count", "lrs_prof_read",
                              "lrs_prof_release")
 
@@ -59,6 +62,8 @@ def load_library() -> ctypes.CDLL:
         else:
             fn.argtypes = [vp, psz, vp, vp, i64, ci, ci, vp]
         fn.restype = ci
+    lib.lrs_sort_digits.argtypes = [ci, ci, vp, psz, vp, vp, vp, vp, i64, ci, ci, vp]
+    lib.lrs_sort_digits.restype = ci
     lib.lrs_status_string.argtypes = [ci]
     lib.lrs_status_string.restype = ctypes.c_char_p
     lib.lrs_device_copy.argtypes = [vp, vp, sz, vp]
@@ -158,6 +163,23 @@ lrs_sort_pairs_i64 = _make_pairs("lrs_sort_pairs_i64")
 lrs_sort_pairs_f64 = _make_pairs("lrs_sort_pairs_f64")
 
 
+def lrs_sort_digits(key_type, digit_bits, d_temp, temp_bytes, d_keys_in, d_values_in, d_keys_out,
+                    d_values_out, n, begin_bit, end_bit, stream=None):
+    """Calls the C function of the same name.  key_type is an lrs_key_type code
+    or a suffix ("u32", ..., "f64"); the value arrays are both None for a
+    keys-only sort.  With d_temp None returns the temp bytes needed."""
+    lib = load_library()
+    code = KEY_TYPE_CODES[key_type] if isinstance(key_type, str) else int(key_type)
+    tb = ctypes.c_size_t(int(temp_bytes or 0))
+    temp = _ptr(d_temp)
+    st = None if temp is None else _stream(stream)
+    status = lib.lrs_sort_digits(code, int(digit_bits), temp, ctypes.byref(tb), _ptr(d_keys_in),
+                                 _ptr(d_values_in), _ptr(d_keys_out), _ptr(d_values_out), int(n),
+                                 int(begin_bit), int(end_bit), st)
+    _check(status, "lrs_sort_digits")
+    return tb.value
+
+
 def lrs_device_copy(d_dst, d_src, nbytes: int, stream=None) -> None:
     _check(load_library().lrs_device_copy(_ptr(d_dst), _ptr(d_src), int(nbytes), _stream(stream)),
            "lrs_device_copy")
@@ -210,16 +232,25 @@ def _temp_tensor(nbytes, device, temp):
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
-def sort_keys(keys, begin_bit: int = 0, end_bit: int | None = None, out=None, temp=None, stream=None):
+def sort_keys(keys, begin_bit: int = 0, end_bit: int | None = None, out=None, temp=None, stream=None,
+              digit_bits: int = 8):
     """Stable ascending sort of a 1-D device tensor of keys (uint32, int32,
     float32, uint64, int64 or float64) over bits [begin_bit, end_bit) of their
-    order code; returns the output tensor."""
+    order code, in passes of `digit_bits` (8 or 11) bits; returns the output
+    tensor."""
     import torch
     sfx = key_suffix(keys.dtype)
     end_bit = KEY_BITS[sfx] if end_bit is None else end_bit
     keys = keys.contiguous()
     if out is None:
         out = torch.empty_like(keys)
+    if digit_bits != 8:
+        n = keys.numel()
+        need = lrs_sort_digits(sfx, digit_bits, None, 0, keys, None, out, None, n, begin_bit, end_bit)
+        t = _temp_tensor(need, keys.device, temp)
+        lrs_sort_digits(sfx, digit_bits, t, t.numel() * t.element_size(), keys, None, out, None, n,
+                        begin_bit, end_bit, stream)
+        return out
     fn = globals()["lrs_sort_keys_" + sfx]
     need = fn(None, 0, keys, out, keys.numel(), begin_bit, end_bit)
     t = _temp_tensor(need, keys.device, temp)
@@ -228,8 +259,9 @@ def sort_keys(keys, begin_bit: int = 0, end_bit: int | None = None, out=None, te
 
 
 def sort_pairs(keys, values, begin_bit: int = 0, end_bit: int | None = None, keys_out=None,
-               values_out=None, temp=None, stream=None):
-    """Stable ascending pair sort (uint32 values); returns (keys_out, values_out)."""
+               values_out=None, temp=None, stream=None, digit_bits: int = 8):
+    """Stable ascending pair sort (uint32 values) in passes of `digit_bits` (8
+    or 11) bits; returns (keys_out, values_out)."""
     import torch
     sfx = key_suffix(keys.dtype)
     if str(values.dtype) != "torch.uint32":
@@ -241,8 +273,15 @@ def sort_pairs(keys, values, begin_bit: int = 0, end_bit: int | None = None, key
         keys_out = torch.empty_like(keys)
     if values_out is None:
         values_out = torch.empty_like(values)
-    fn = globals()["lrs_sort_pairs_" + sfx]
     n = keys.numel()
+    if digit_bits != 8:
+        need = lrs_sort_digits(sfx, digit_bits, None, 0, keys, values, keys_out, values_out, n, begin_bit,
+                               end_bit)
+        t = _temp_tensor(need, keys.device, temp)
+        lrs_sort_digits(sfx, digit_bits, t, t.numel() * t.element_size(), keys, values, keys_out,
+                        values_out, n, begin_bit, end_bit, stream)
+        return keys_out, values_out
+    fn = globals()["lrs_sort_pairs_" + sfx]
     need = fn(None, 0, keys, values, keys_out, values_out, n, begin_bit, end_bit)
     t = _temp_tensor(need, keys.device, temp)
     fn(t, t.numel() * t.element_size(), keys, values, keys_out, values_out, n, begin_bit, end_bit, stream)

@@ -114,24 +114,25 @@ __device__ __forceinline__ uint32_t bit_mask(uint32_t d)
 // the blog.csdn.net page about the qsort_warp sample).  All 64 lanes must be
 // active.  v_bitop3 0x90 computes m & ~(ballot ^ t): with t all-ones when our
 // bit is set it keeps the ballot, otherwise its complement.  Four VALU
-// instructions per digit bit.
-template <int B = 0>
+// instructions per digit bit; BITS is the digit width.
+template <int BITS, int B = 0>
 __device__ __forceinline__ void match_bits(uint32_t d, uint32_t &lo, uint32_t &hi)
 {
-    if constexpr (B < kRadixBits) {
+    if constexpr (B < BITS) {
         const uint32_t t = bit_mask<B>(d);
         const uint64_t bal = __ballot(t != 0u);
         lo = __builtin_amdgcn_bitop3_b32(lo, (uint32_t)bal, t, 0x90);
         hi = __builtin_amdgcn_bitop3_b32(hi, (uint32_t)(bal >> 32), t, 0x90);
-        match_bits<B + 1>(d, lo, hi);
+        match_bits<BITS, B + 1>(d, lo, hi);
     }
 }
 
+template <int BITS = kRadixBits>
 __device__ __forceinline__ void match_digit(uint32_t d, uint32_t &lo, uint32_t &hi)
 {
     lo = 0xFFFFFFFFu;
     hi = 0xFFFFFFFFu;
-    match_bits<0>(d, lo, hi);
+    match_bits<BITS>(d, lo, hi);
 }
 
 // Number of set bits of (hi:lo) in lanes below this one.
@@ -273,7 +274,8 @@ __device__ __forceinline__ void count_range(const K *__restrict__ keys, int64_t 
 // within a wave (the kwkr.cn essay, section 3.2, and the quant67.com survey,
 // section 8.1: per-block and per-warp counting instead of global atomics).
 // The keys are read 16 bytes per lane when their array is 16-byte aligned.
-template <typename K, int CODE, int THREADS>
+// RB is the digit width: 8, or 11 for the 2048-digit passes.
+template <typename K, int CODE, int THREADS, int RB = kRadixBits>
 __global__ __launch_bounds__(THREADS) void upsweep_kernel(
     SortBufs bufs, const uint32_t *__restrict__ route, int pass, int src_fixed, uint32_t *__restrict__ counts,
     int64_t n, int64_t block_len, int num_blocks, int shift, uint32_t mask)
@@ -292,9 +294,11 @@ __global__ __launch_bounds__(THREADS) void upsweep_kernel(
     constexpr int WAVES = THREADS / kWave;
     // COPIES sub-histograms per wave (lane % COPIES picks one), padded by one
     // word so that equal digits in different copies fall in different banks:
-    // skewed digits then serialize at most 64/COPIES lanes per atomic.
-    constexpr int COPIES = 4;
-    constexpr int STRIDE = kRadix + 1;
+    // skewed digits then serialize at most 64/COPIES lanes per atomic.  With
+    // 2048 digits one copy per wave (64 KB in all) is what LDS holds.
+    constexpr int RADIX = 1 << RB;
+    constexpr int COPIES = RB == kRadixBits ? 4 : 1;
+    constexpr int STRIDE = RADIX + 1;
     __shared__ uint32_t hist[WAVES * COPIES][STRIDE];
     const int tid = threadIdx.x;
     uint32_t *h = hist[(tid / kWave) * COPIES + (tid % COPIES)];
@@ -307,7 +311,7 @@ __global__ __launch_bounds__(THREADS) void upsweep_kernel(
     count_range<K, CODE, THREADS>(keys, begin, end, h, tid, shift, mask);
     __syncthreads();
 
-    for (int d = tid; d < kRadix; d += THREADS) {
+    for (int d = tid; d < RADIX; d += THREADS) {
         uint32_t s = 0;
 #pragma unroll
         for (int w = 0; w < WAVES * COPIES; ++w) s += hist[w][d];
@@ -916,6 +920,241 @@ __global__ __launch_bounds__(WAVES *kWave)
         process_tile(a, ta, 0, false);
         ready(b);
         process_tile(b, ta + TILE, 1, true);
+    }
+}
+
+// ------------------------------------------------------ 2048-digit downsweep
+//
+// The downsweep of an 11-bit pass (2048 digits; three passes cover 32 bits
+// instead of four: the kwkr.cn essay on bitonic vs. LSD radix sort, sections
+// 3.4 and 5.2, and the page "GPU radix sort: from the CUB implementation to
+// performance tuning", section 4, on the pass count against the cost of more
+// buckets).  Same tile order and stable rank as the 8-bit downsweep, with
+// what 2048 digits change:
+//  - the match takes 11 ballots;
+//  - per-wave counters cover 2048 digits (4 KB per wave), one buffer;
+//  - the digit offsets of a tile come from a workgroup-wide scan, each thread
+//    owning 4 digits and keeping their running output indices in registers;
+//  - there is no write-combining carry (one open line per digit would take
+//    256 KB of LDS): a tile's keys go from LDS straight to their output
+//    positions, a digit's run of about 4 keys at a time.
+// Eight waves, 16 keys per lane: 8,192-key tiles.
+constexpr int kWideDigitWaves = 8;
+constexpr int kWideDigitItems = 16;
+
+template <typename K, bool PAIRS, int RB>
+struct WideDigitSmem {
+    static constexpr int kRadixW = 1 << RB;
+    static constexpr int kTile = kWideDigitWaves * kWave * kWideDigitItems;
+    K keys[kTile];                     // the tile in digit order
+    uint32_t vals[PAIRS ? kTile : 1];  // payload in the same order
+    // Per wave and digit: the tile's 16-bit counts, then (after the tile's
+    // scan) the tile slot of the wave's first key of the digit.
+    alignas(16) uint16_t wave_count[kWideDigitWaves][kRadixW];
+    alignas(16) uint32_t place[kRadixW];  // output index of tile slot 0 of digit d (mod 2^32)
+    uint32_t scan_tmp[kWideDigitWaves];
+};
+
+// Waves per SIMD for the register allocation: 32-bit keys alone fit two
+// workgroups per CU in LDS.
+template <typename K, bool PAIRS>
+constexpr int wide_digit_waves_per_simd()
+{
+    return sizeof(K) == 4 && !PAIRS ? 4 : 2;
+}
+
+template <typename K, bool PAIRS, int RB, int CODE, bool WIDE>
+__global__ __launch_bounds__(kWideDigitWaves *kWave)
+    __attribute__((amdgpu_waves_per_eu(wide_digit_waves_per_simd<K, PAIRS>()))) void wide_digit_downsweep_kernel(
+        SortBufs bufs, uint32_t *__restrict__ route_k, uint32_t *__restrict__ route_v, int pass, int ksrc_fixed,
+        int vsrc_fixed, int kplanned, int vplanned, int last, const uint32_t *__restrict__ counts,
+        const uint32_t *__restrict__ row_total, int64_t n, int64_t block_len, int count_cols, int split, int shift,
+        uint32_t mask)
+{
+    using Smem = WideDigitSmem<K, PAIRS, RB>;
+    constexpr int RADIX = Smem::kRadixW;
+    constexpr int THREADS = kWideDigitWaves * kWave;
+    constexpr int ITEMS = kWideDigitItems;
+    constexpr int TILE = Smem::kTile;
+    constexpr int WAVE_KEYS = kWave * ITEMS;
+    static_assert(RADIX == 4 * THREADS, "each thread owns four digits");
+    static_assert(TILE < 65536, "16-bit counts and slots");
+    __shared__ Smem s;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int blk = blockIdx.x;
+    const int64_t blk_begin = (int64_t)blk * block_len;
+    const int64_t blk_end = blk_begin + block_len < n ? blk_begin + block_len : n;
+    const uint32_t n32 = (uint32_t)n;
+
+    const int ksrc = pass_source(route_k, pass, ksrc_fixed);
+    const int vsrc = PAIRS ? pass_source(route_v, pass, vsrc_fixed) : 0;
+    const K *__restrict__ keys_in = (const K *)bufs.keys[ksrc];
+
+    // This thread's digits 4*tid .. 4*tid+3: their totals, and the block's
+    // prefix within each (the count column of the block's first sub-block).
+    const uint4 tot4 = reinterpret_cast<const uint4 *>(row_total)[tid];
+    uint32_t run[4];
+    {
+        const int64_t col = (int64_t)blk * split;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) run[k] = counts[(int64_t)(4 * tid + k) * count_cols + col];
+    }
+    // The pass is skipped when one digit holds every key.
+    const bool skip =
+        __syncthreads_or(tot4.x == n32 || tot4.y == n32 || tot4.z == n32 || tot4.w == n32) != 0;
+    const int kdst = pass_dest(ksrc, kplanned, last != 0, skip);
+    const int vdst = PAIRS ? pass_dest(vsrc, vplanned, last != 0, skip) : 0;
+    if (blk == 0 && tid == 0) {
+        route_k[pass + 1] = (uint32_t)kdst;
+        if constexpr (PAIRS) route_v[pass + 1] = (uint32_t)vdst;
+    }
+    if (skip) return;
+    K *__restrict__ keys_out = (K *)bufs.keys[kdst];
+    const uint32_t *__restrict__ vals_in = PAIRS ? bufs.vals[vsrc] : nullptr;
+    uint32_t *__restrict__ vals_out = PAIRS ? (uint32_t *)bufs.vals[vdst] : nullptr;
+
+    // The block's first output index of each owned digit: the digit's start
+    // (exclusive prefix of the totals over all digits) plus the block prefix.
+    {
+        uint32_t all;
+        const uint32_t start = block_exclusive_scan<THREADS>(tot4.x + tot4.y + tot4.z + tot4.w, s.scan_tmp, all);
+        run[0] += start;
+        run[1] += start + tot4.x;
+        run[2] += start + tot4.x + tot4.y;
+        run[3] += start + tot4.x + tot4.y + tot4.z;
+    }
+
+    auto ready = [](K(&kb)[ITEMS]) {
+#pragma unroll
+        for (int i = 0; i < ITEMS; ++i) asm volatile("" : "+v"(kb[i]));
+    };
+    auto lane_first = [&]() {
+        int tid_l = tid;
+        asm volatile("" : "+v"(tid_l));
+        return (tid_l / kWave) * WAVE_KEYS + (tid_l & (kWave - 1));
+    };
+    const __amdgpu_buffer_rsrc_t keys_buf =
+        buffer_over(keys_in + blk_begin, (uint32_t)((blk_end - blk_begin) * (int64_t)sizeof(K)));
+    const __amdgpu_buffer_rsrc_t vals_buf =
+        buffer_over(PAIRS ? vals_in + blk_begin : nullptr, PAIRS ? (uint32_t)((blk_end - blk_begin) * 4) : 0u);
+    const __amdgpu_buffer_rsrc_t kout_buf = buffer_over(keys_out, WIDE ? 0u : (uint32_t)(n * (int64_t)sizeof(K)));
+    const __amdgpu_buffer_rsrc_t vout_buf = buffer_over(vals_out, PAIRS && !WIDE ? n32 * 4u : 0u);
+    auto prefetch = [&](K(&kb)[ITEMS], int64_t tile_begin) {
+        issue_tile_loads<K, ITEMS>(kb, keys_buf, (uint32_t)(tile_begin - blk_begin), lane_first());
+    };
+
+    auto process_tile = [&](K(&kb)[ITEMS], int64_t tile_begin) {
+        const int valid = blk_end - tile_begin < TILE ? (int)(blk_end - tile_begin) : TILE;
+        const bool full = valid == TILE;
+        const int first = lane_first();
+        uint32_t v[ITEMS];
+        if constexpr (PAIRS) issue_tile_loads<uint32_t, ITEMS>(v, vals_buf, (uint32_t)(tile_begin - blk_begin), first);
+        finish_tile<K, CODE, ITEMS>(kb, first, valid, full);
+
+        // This wave's counters start at zero.  Its row was last read by this
+        // wave's scatter in the previous tile, and by every thread's scan
+        // before that tile's second barrier.
+        uint16_t *const row = s.wave_count[wave];
+#pragma unroll
+        for (int q = 0; q < RADIX / (8 * kWave); ++q)
+            reinterpret_cast<uint4 *>(row)[q * kWave + lane] = make_uint4(0u, 0u, 0u, 0u);
+
+        // Rank within the wave, as in the 8-bit downsweep.
+        uint32_t r[ITEMS];
+#pragma unroll
+        for (int i = 0; i < ITEMS; ++i) {
+            const uint32_t d = digit_of<CODE>(kb[i], shift, mask);
+            uint16_t *counter = row + d;
+            const uint32_t prior = *counter;
+            uint32_t lo, hi;
+            match_digit<RB>(d, lo, hi);
+            uint32_t part = __popc(lo) + prior;
+            asm volatile("" : "+v"(part));
+            *counter = (uint16_t)(__popc(hi) + part);
+            r[i] = __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, prior));
+            asm volatile("" : "+v"(r[i]));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __syncthreads();
+
+        // Thread t's digits 4t..4t+3: each wave's prefix over the waves before
+        // it (two 16-bit counts per word; a digit's tile total is below 2^16),
+        // the tile's totals, and their exclusive prefix over all digits.
+        uint2 pre[kWideDigitWaves];
+        uint2 sum = make_uint2(0u, 0u);
+#pragma unroll
+        for (int w = 0; w < kWideDigitWaves; ++w) {
+            const uint2 c = reinterpret_cast<const uint2 *>(s.wave_count[w])[tid];
+            pre[w] = sum;
+            sum.x += c.x;
+            sum.y += c.y;
+        }
+        const uint32_t t0 = sum.x & 0xFFFFu, t1 = sum.x >> 16, t2 = sum.y & 0xFFFFu, t3 = sum.y >> 16;
+        uint32_t all;
+        const uint32_t o0 = block_exclusive_scan<THREADS>(t0 + t1 + t2 + t3, s.scan_tmp, all);
+        const uint32_t o1 = o0 + t0, o2 = o1 + t1, o3 = o2 + t2;
+        // Slot bases (only this thread touches these four columns), and the
+        // output index of tile slot 0 of each digit.
+        const uint2 off = make_uint2(o0 | (o1 << 16), o2 | (o3 << 16));
+#pragma unroll
+        for (int w = 0; w < kWideDigitWaves; ++w)
+            reinterpret_cast<uint2 *>(s.wave_count[w])[tid] = make_uint2(off.x + pre[w].x, off.y + pre[w].y);
+        reinterpret_cast<uint4 *>(s.place)[tid] = make_uint4(run[0] - o0, run[1] - o1, run[2] - o2, run[3] - o3);
+        run[0] += t0;
+        run[1] += t1;
+        run[2] += t2;
+        run[3] += t3;
+        __syncthreads();
+
+        // Reorder the tile in LDS.
+#pragma unroll
+        for (int i = 0; i < ITEMS; ++i) r[i] += row[digit_of<CODE>(kb[i], shift, mask)];
+#pragma unroll
+        for (int i = 0; i < ITEMS; ++i) {
+            s.keys[r[i]] = kb[i];
+            if constexpr (PAIRS) s.vals[r[i]] = v[i];
+        }
+        __syncthreads();
+
+        // Store: consecutive threads take consecutive tile slots, so each
+        // digit's run goes out as consecutive addresses.  Slots past `valid`
+        // hold the padding keys (largest digit, after every real key).
+#pragma unroll
+        for (int i = 0; i < ITEMS; ++i) {
+            const int j = i * THREADS + tid;
+            const K x = s.keys[j];
+            const uint32_t pos = s.place[digit_of<CODE>(x, shift, mask)] + (uint32_t)j;
+            const bool put = j < valid;
+            store_out<WIDE>(x, keys_out, kout_buf, pos, put);
+            if constexpr (PAIRS) store_out<WIDE>(s.vals[j], vals_out, vout_buf, pos, put);
+        }
+    };
+
+    // One tile ahead, as in the 8-bit downsweep.
+    K a[ITEMS], b[ITEMS];
+    prefetch(a, blk_begin);
+    ready(a);
+    const int tiles = (int)((blk_end - blk_begin + TILE - 1) / TILE);
+    const int pairs = (tiles - 1) / 2;
+    int64_t ta = blk_begin;
+    for (int p = 0; p < pairs; ++p, ta += 2 * TILE) {
+        prefetch(b, ta + TILE);
+        process_tile(a, ta);
+        ready(b);
+        prefetch(a, ta + 2 * TILE);
+        process_tile(b, ta + TILE);
+        ready(a);
+    }
+    if (tiles - 2 * pairs == 1) {
+        process_tile(a, ta);
+    } else {
+        prefetch(b, ta + TILE);
+        process_tile(a, ta);
+        ready(b);
+        process_tile(b, ta + TILE);
     }
 }
 

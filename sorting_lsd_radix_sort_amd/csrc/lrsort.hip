@@ -41,6 +41,7 @@ int key_code(KeyKind k)
 }
 
 constexpr int kMaxBlocks = 4096;  // count-matrix width cap (scan: 256 threads x 16)
+constexpr int kWideDigitBits = 11;  // the other digit width lrs_sort_digits takes
 constexpr int kMaxSplit = 8;      // upsweep sub-blocks per downsweep block
 constexpr int kMaxRoute = 16;     // route entries per array: passes + 1 (at most 9)
 constexpr int kUpsweepThreads = 512;
@@ -204,6 +205,7 @@ struct Request {
     uint32_t *vals_out;
     int64_t n;
     int begin_bit, end_bit;
+    int digit_bits = kRadixBits;  // 8, or 11 (2048-digit passes)
 };
 
 struct Layout {
@@ -220,17 +222,19 @@ Layout make_layout(const Request &rq)
 {
     Layout L;
     const size_t ksz = (size_t)key_bytes(rq.kind);
-    L.passes = (rq.end_bit - rq.begin_bit + kRadixBits - 1) / kRadixBits;
-    L.tile = tile_keys(rq.kind, rq.vals_in != nullptr, rq.n);
+    const size_t radix = (size_t)1 << rq.digit_bits;
+    L.passes = (rq.end_bit - rq.begin_bit + rq.digit_bits - 1) / rq.digit_bits;
+    L.tile = rq.digit_bits == kRadixBits ? tile_keys(rq.kind, rq.vals_in != nullptr, rq.n)
+                                         : kWideDigitWaves * 64 * kWideDigitItems;
     L.tiles = (rq.n + L.tile - 1) / L.tile;
     L.max_cols = (int)std::min<int64_t>(L.tiles * kMaxSplit, kMaxBlocks);
     L.kplan = make_plan(L.passes, rq.keys_in == rq.keys_out);
     L.vplan = make_plan(L.passes, rq.vals_in != nullptr && rq.vals_in == rq.vals_out);
     size_t off = 0;
     L.off_counts = off;
-    off += align_up((size_t)kRadix * L.max_cols * 4);
+    off += align_up(radix * L.max_cols * 4);
     L.off_rowtot = off;
-    off += align_up((size_t)kRadix * 4);
+    off += align_up(radix * 4);
     L.off_route = off;  // where keys, then values, are before each pass and at the end
     off += align_up((size_t)2 * kMaxRoute * 4);
     const size_t kbytes = align_up((size_t)rq.n * ksz), vbytes = align_up((size_t)rq.n * 4);
@@ -277,21 +281,22 @@ lrs_status copy_bytes(void *dst, const void *src, size_t bytes, hipStream_t stre
 
 // ------------------------------------------------------------ pass launchers
 
-template <typename K, int CODE>
+template <typename K, int CODE, int RB>
 hipError_t launch_upsweep(const SortBufs &bufs, const uint32_t *route, int pass, int src_fixed, uint32_t *counts,
                           int64_t n, int64_t block_len, int blocks, int shift, uint32_t mask, hipStream_t stream)
 {
     return launch(LRS_KERNEL_UPSWEEP, stream, [&] {
         const int grid = (blocks + kXcds - 1) / kXcds * kXcds;  // see upsweep_kernel's column mapping
-        upsweep_kernel<K, CODE, kUpsweepThreads><<<grid, kUpsweepThreads, 0, stream>>>(
+        upsweep_kernel<K, CODE, kUpsweepThreads, RB><<<grid, kUpsweepThreads, 0, stream>>>(
             bufs, route, pass, src_fixed, counts, n, block_len, blocks, shift, mask);
     });
 }
 
-hipError_t launch_scan(uint32_t *counts, uint32_t *rowtot, int blocks, hipStream_t stream)
+// One workgroup per digit (row of the count matrix).
+hipError_t launch_scan(uint32_t *counts, uint32_t *rowtot, int blocks, int radix, hipStream_t stream)
 {
     return launch(LRS_KERNEL_SCAN, stream, [&] {
-        scan_kernel<kScanThreads, kScanPerThread><<<kRadix, kScanThreads, 0, stream>>>(counts, rowtot, blocks);
+        scan_kernel<kScanThreads, kScanPerThread><<<radix, kScanThreads, 0, stream>>>(counts, rowtot, blocks);
     });
 }
 
@@ -303,10 +308,14 @@ bool wide_output(int64_t n)
     return n * (int64_t)sizeof(K) > ((int64_t)1 << 31);
 }
 
-template <typename K, bool PAIRS, int WAVES, int ITEMS, int CODE>
+template <typename K, bool PAIRS, int WAVES, int ITEMS, int CODE, int RB = kRadixBits>
 auto downsweep_fn(bool wide)
 {
-    if constexpr (ITEMS == kSmallItems) {
+    if constexpr (RB != kRadixBits) {
+        static_assert(WAVES == kWideDigitWaves && ITEMS == kWideDigitItems, "the 2048-digit downsweep's shape");
+        return wide ? wide_digit_downsweep_kernel<K, PAIRS, RB, CODE, true>
+                    : wide_digit_downsweep_kernel<K, PAIRS, RB, CODE, false>;
+    } else if constexpr (ITEMS == kSmallItems) {
         return downsweep_kernel<K, PAIRS, WAVES, ITEMS, CODE, false>;  // small n: never wide
     } else {
         return wide ? downsweep_kernel<K, PAIRS, WAVES, ITEMS, CODE, true>
@@ -321,26 +330,26 @@ struct PassRoute {
     int last;
 };
 
-template <typename K, bool PAIRS, int WAVES, int ITEMS, int CODE>
+template <typename K, bool PAIRS, int WAVES, int ITEMS, int CODE, int RB>
 hipError_t launch_downsweep(const SortBufs &bufs, uint32_t *route_k, uint32_t *route_v, const PassRoute &pr,
                             const uint32_t *counts, const uint32_t *rowtot, int64_t n, int64_t block_len,
                             int blocks, int cols, int split, int shift, uint32_t mask, hipStream_t stream)
 {
     return launch(LRS_KERNEL_DOWNSWEEP, stream, [&] {
-        downsweep_fn<K, PAIRS, WAVES, ITEMS, CODE>(wide_output<K>(n))<<<blocks, WAVES * 64, 0, stream>>>(
+        downsweep_fn<K, PAIRS, WAVES, ITEMS, CODE, RB>(wide_output<K>(n))<<<blocks, WAVES * 64, 0, stream>>>(
             bufs, route_k, route_v, pr.pass, pr.ksrc_fixed, pr.vsrc_fixed, pr.kplanned, pr.vplanned, pr.last,
             counts, rowtot, n, block_len, cols, split, shift, mask);
     });
 }
 
 // The kernel whose occupancy sets the number of blocks for this key type.
-template <typename K, bool PAIRS, int WAVES, int ITEMS, int CODE>
+template <typename K, bool PAIRS, int WAVES, int ITEMS, int CODE, int RB>
 hipError_t blocks_for(int64_t n, int64_t tiles, int *blocks)
 {
     int cus = 0, per_cu = 0;
     hipError_t err = device_cus(&cus);
     if (err != hipSuccess) return err;
-    err = occupancy((const void *)downsweep_fn<K, PAIRS, WAVES, ITEMS, CODE>(wide_output<K>(n)), WAVES * 64,
+    err = occupancy((const void *)downsweep_fn<K, PAIRS, WAVES, ITEMS, CODE, RB>(wide_output<K>(n)), WAVES * 64,
                     &per_cu);
     if (err != hipSuccess) return err;
     // The downsweep reads a block's keys through a buffer whose size field is
@@ -369,12 +378,13 @@ SortBufs sort_bufs(const Request &rq, const Layout &L, char *temp)
     return bufs;
 }
 
-template <typename K, bool PAIRS, int WAVES, int ITEMS, int CODE>
+// RB: digit width (8, or 11 with the 2048-digit downsweep).
+template <typename K, bool PAIRS, int WAVES, int ITEMS, int CODE, int RB = kRadixBits>
 lrs_status run_passes(const Request &rq, const Layout &L, char *temp, hipStream_t stream)
 {
     constexpr int TILE = WAVES * 64 * ITEMS;
     int want_blocks = 0;
-    if (blocks_for<K, PAIRS, WAVES, ITEMS, CODE>(rq.n, L.tiles, &want_blocks) != hipSuccess) return LRS_ERR_HIP;
+    if (blocks_for<K, PAIRS, WAVES, ITEMS, CODE, RB>(rq.n, L.tiles, &want_blocks) != hipSuccess) return LRS_ERR_HIP;
     const int64_t tiles_per_block = (L.tiles + want_blocks - 1) / want_blocks;
     const int64_t block_len = tiles_per_block * TILE;
     const int blocks = (int)((rq.n + block_len - 1) / block_len);
@@ -383,7 +393,7 @@ lrs_status run_passes(const Request &rq, const Layout &L, char *temp, hipStream_
     // occupancy allows; the count matrix has one column per sub-block.
     int cus = 0, up_per_cu = 0;
     if (device_cus(&cus) != hipSuccess) return LRS_ERR_HIP;
-    if (occupancy((const void *)upsweep_kernel<K, CODE, kUpsweepThreads>, kUpsweepThreads, &up_per_cu) !=
+    if (occupancy((const void *)upsweep_kernel<K, CODE, kUpsweepThreads, RB>, kUpsweepThreads, &up_per_cu) !=
         hipSuccess)
         return LRS_ERR_HIP;
     int split = 1;
@@ -403,8 +413,8 @@ lrs_status run_passes(const Request &rq, const Layout &L, char *temp, hipStream_
     const int vstart = PAIRS && rq.vals_in == rq.vals_out ? BUF_OUT : BUF_IN;
 
     for (int p = 0; p < L.passes; ++p) {
-        const int shift = rq.begin_bit + kRadixBits * p;
-        const int width = std::min(kRadixBits, rq.end_bit - shift);
+        const int shift = rq.begin_bit + RB * p;
+        const int width = std::min(RB, rq.end_bit - shift);
         const uint32_t mask = (1u << width) - 1u;
         PassRoute pr;
         pr.pass = p;
@@ -414,12 +424,12 @@ lrs_status run_passes(const Request &rq, const Layout &L, char *temp, hipStream_
         pr.vplanned = L.vplan.dst[p];
         pr.last = p == L.passes - 1;
 
-        hipError_t err = launch_upsweep<K, CODE>(bufs, route_k, p, pr.ksrc_fixed, counts, rq.n, sub_len, cols, shift,
-                                                 mask, stream);
+        hipError_t err = launch_upsweep<K, CODE, RB>(bufs, route_k, p, pr.ksrc_fixed, counts, rq.n, sub_len, cols,
+                                                     shift, mask, stream);
         if (err != hipSuccess) return LRS_ERR_HIP;
-        if (launch_scan(counts, rowtot, cols, stream) != hipSuccess) return LRS_ERR_HIP;
-        err = launch_downsweep<K, PAIRS, WAVES, ITEMS, CODE>(bufs, route_k, route_v, pr, counts, rowtot, rq.n,
-                                                             block_len, blocks, cols, split, shift, mask, stream);
+        if (launch_scan(counts, rowtot, cols, 1 << RB, stream) != hipSuccess) return LRS_ERR_HIP;
+        err = launch_downsweep<K, PAIRS, WAVES, ITEMS, CODE, RB>(bufs, route_k, route_v, pr, counts, rowtot, rq.n,
+                                                                 block_len, blocks, cols, split, shift, mask, stream);
         if (err != hipSuccess) return LRS_ERR_HIP;
     }
     // The data is in the output unless skipped passes left it elsewhere (or a
@@ -447,6 +457,10 @@ lrs_status run_kind(bool pairs, const Request &r, const Layout &L, char *temp, h
 {
     if (pairs && r.n <= tiny_max<K, true>()) return run_tiny<K, true, CODE>(r, stream);
     if (!pairs && r.n <= tiny_max<K, false>()) return run_tiny<K, false, CODE>(r, stream);
+    if (r.digit_bits == kWideDigitBits) {
+        if (pairs) return run_passes<K, true, kWideDigitWaves, kWideDigitItems, CODE, kWideDigitBits>(r, L, temp, stream);
+        return run_passes<K, false, kWideDigitWaves, kWideDigitItems, CODE, kWideDigitBits>(r, L, temp, stream);
+    }
     if (r.n <= kSmallTileMaxKeys) {
         if (pairs) return run_passes<K, true, 8, kSmallItems, CODE>(r, L, temp, stream);
         return run_passes<K, false, 8, kSmallItems, CODE>(r, L, temp, stream);
@@ -462,6 +476,7 @@ lrs_status sort_entry(const Request &rq, void *d_temp, size_t *temp_bytes, hipSt
 {
     // All checks happen before any HIP call, so they need no device.
     if (temp_bytes == nullptr) return LRS_ERR_INVALID_ARG;
+    if (rq.digit_bits != kRadixBits && rq.digit_bits != kWideDigitBits) return LRS_ERR_INVALID_ARG;
     const int key_bits = 8 * key_bytes(rq.kind);
     const size_t ksz = key_bits / 8;
     if (rq.n < 0 || rq.n > (int64_t)0xFFFFFFFFll) return LRS_ERR_INVALID_ARG;
@@ -603,6 +618,26 @@ LRS_API lrs_status lrs_sort_pairs_f64(void *d_temp, size_t *temp_bytes, const do
     if (n > 0 && (!d_values_in || !d_values_out)) return LRS_ERR_INVALID_ARG;
     return sort_entry({KIND_F64, d_keys_in, d_keys_out, d_values_in, d_values_out, n, begin_bit, end_bit}, d_temp,
                       temp_bytes, stream);
+}
+
+LRS_API lrs_status lrs_sort_digits(lrs_key_type key_type, int digit_bits, void *d_temp, size_t *temp_bytes,
+                                   const void *d_keys_in, const uint32_t *d_values_in, void *d_keys_out,
+                                   uint32_t *d_values_out, int64_t n, int begin_bit, int end_bit, hipStream_t stream)
+{
+    KeyKind kind;
+    switch (key_type) {
+    case LRS_KEY_U32: kind = KIND_U32; break;
+    case LRS_KEY_I32: kind = KIND_I32; break;
+    case LRS_KEY_F32: kind = KIND_F32; break;
+    case LRS_KEY_U64: kind = KIND_U64; break;
+    case LRS_KEY_I64: kind = KIND_I64; break;
+    case LRS_KEY_F64: kind = KIND_F64; break;
+    default: return LRS_ERR_INVALID_ARG;
+    }
+    if (n > 0 && (d_values_in == nullptr) != (d_values_out == nullptr)) return LRS_ERR_INVALID_ARG;
+    Request rq{kind, d_keys_in, d_keys_out, d_values_in, d_values_out, n, begin_bit, end_bit};
+    rq.digit_bits = digit_bits;
+    return sort_entry(rq, d_temp, temp_bytes, stream);
 }
 
 LRS_API const char *lrs_status_string(lrs_status status)

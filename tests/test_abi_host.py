@@ -139,3 +139,55 @@ def test_device_copy_and_prof_argument_checks():
     k, ms = ctypes.c_int(), ctypes.c_float()
     assert lib.lrs_prof_read(0, ctypes.byref(k), ctypes.byref(ms)) == lrs.LRS_ERR_INVALID_ARG
     assert lib.lrs_prof_release() == lrs.LRS_OK
+
+
+def q_digits(sfx, digit_bits, n, b, e, kin=A, vin=None, kout=B, vout=None):
+    return lrs.lrs_sort_digits(sfx, digit_bits, None, 0, kin, vin, kout, vout, n, b, e)
+
+
+@pytest.mark.parametrize("sfx,ksz,bits", [("u32", 4, 32), ("f32", 4, 32), ("u64", 8, 64), ("i64", 8, 64)])
+def test_digit_width_temp_queries(sfx, ksz, bits):
+    n = 100_000_000
+    # 8-bit digits through the generic call ask what the typed call asks
+    assert q_digits(sfx, 8, n, 0, bits) == q_keys(sfx, n, 0, bits)
+    assert q_digits(sfx, 8, n, 0, bits, vin=C, vout=D) == q_pairs(sfx, n, 0, bits)
+    # 11-bit digits: the same alternate buffers plus a count matrix 8 times
+    # larger (2048 rows, at most 4096 columns of 4 bytes)
+    t11 = q_digits(sfx, 11, n, 0, bits)
+    assert ksz * n <= t11 <= ksz * n + 40 * 2**20
+    assert t11 > q_keys(sfx, n, 0, bits)
+    # one 11-bit pass covers [0, 11): no alternate buffer out of place
+    assert q_digits(sfx, 11, n, 0, 11) <= 40 * 2**20
+    # ... and in place it goes through one alternate and is copied back
+    assert q_digits(sfx, 11, n, 0, 11, kin=A, kout=A) >= ksz * n
+    # in place, 3 passes (33 bits or fewer in 11-bit digits) need two alternates
+    t3 = q_digits(sfx, 11, n, 0, 32, kin=A, kout=A)
+    assert 2 * ksz * n <= t3 <= 2 * ksz * n + 40 * 2**20
+    # ... where 8-bit digits over 32 bits (4 passes) need one
+    assert q_keys(sfx, n, 0, 32, kin=A, kout=A) <= ksz * n + 8 * 2**20
+
+
+def test_digit_width_argument_checks():
+    lib = lrs.load_library()
+    tb = ctypes.c_size_t(0)
+    for bits in (0, 4, 7, 9, 10, 12, 16, -8):
+        st = lib.lrs_sort_digits(0, bits, None, ctypes.byref(tb), A, None, B, None, 100, 0, 32, None)
+        assert st == lrs.LRS_ERR_INVALID_ARG, bits
+    for key_type in (-1, 6, 99):
+        st = lib.lrs_sort_digits(key_type, 11, None, ctypes.byref(tb), A, None, B, None, 100, 0, 32, None)
+        assert st == lrs.LRS_ERR_INVALID_ARG, key_type
+    # one value pointer without the other
+    for vin, vout in ((C, None), (None, D)):
+        st = lib.lrs_sort_digits(0, 11, None, ctypes.byref(tb), A, vin, B, vout, 100, 0, 32, None)
+        assert st == lrs.LRS_ERR_INVALID_ARG
+    # the usual checks apply: bit range, alignment, NULL temp_bytes
+    assert lib.lrs_sort_digits(0, 11, None, ctypes.byref(tb), A, None, B, None, 100, 0, 33, None) == \
+        lrs.LRS_ERR_INVALID_ARG
+    assert lib.lrs_sort_digits(3, 11, None, ctypes.byref(tb), A + 4, None, B, None, 100, 0, 64, None) == \
+        lrs.LRS_ERR_INVALID_ARG
+    assert lib.lrs_sort_digits(0, 11, None, None, A, None, B, None, 100, 0, 32, None) == lrs.LRS_ERR_INVALID_ARG
+    # a too-small temp is refused before any device work
+    need = q_digits("u32", 11, 1_000_000, 0, 32)
+    st = lib.lrs_sort_digits(0, 11, ctypes.c_void_p(T), ctypes.byref(ctypes.c_size_t(need - 1)), A, None, B,
+                             None, 1_000_000, 0, 32, None)
+    assert st == lrs.LRS_ERR_TEMP_TOO_SMALL

@@ -1,0 +1,180 @@
+"""Parity of the 11-bit-digit sort (lrs_sort_digits with digit_bits 11) with
+the CPU oracle, on cuda:0.
+
+The oracle does not depend on the digit width: a stable sort of the keys'
+order codes over [begin_bit, end_bit) is one permutation, whatever passes
+reach it.  So the 11-bit path is compared element by element with the same
+oracle as the 8-bit one, over bit ranges that end on, inside and across 11-bit
+digit boundaries (last digits of 1 to 11 bits), at sizes around the
+2048-digit downsweep's 8,192-key tiles and its blocks, plus the properties
+that pin the stable sort at sizes the oracle does not reach.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import checks
+import oracle
+from gpu_util import announce, gpu_sort
+from sorting_lsd_radix_sort_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+D = 11            # digit width under test
+TILE = 8192       # keys per tile of the 2048-digit downsweep
+CUS = 256
+# largest n sorted by one workgroup (that path ignores the digit width)
+TINY_MAX = {(4, False): 16384, (4, True): 8192, (8, False): 8192, (8, True): 4096}
+KEY_TYPES = ["u32", "i32", "f32", "u64", "i64", "f64"]
+RANGES = {"u32": [(0, 32), (0, 11), (0, 22), (0, 23), (3, 17), (5, 27), (21, 32), (31, 32), (5, 5)],
+          "i32": [(0, 32), (0, 22), (10, 32), (31, 32)],
+          "f32": [(0, 32), (0, 20), (16, 32), (31, 32)],
+          "u64": [(0, 64), (0, 33), (7, 60), (53, 64), (63, 64)],
+          "i64": [(0, 64), (32, 64), (5, 61)],
+          "f64": [(0, 64), (0, 40), (44, 64)]}
+
+
+def _compare(keys, vals, b, e, **kw):
+    got_k, got_v = gpu_sort(keys, vals, b, e, digit_bits=D, **kw)
+    if vals is None:
+        want_k = oracle.sort_keys(keys, b, e)
+    else:
+        want_k, want_v = oracle.sort_pairs(keys, vals, b, e)
+        j = checks.first_mismatch(got_v, want_v)
+        assert j < 0, "value mismatch at %d (n=%d, bits [%d,%d))" % (j, keys.size, b, e)
+    i = checks.first_mismatch(got_k, want_k)
+    assert i < 0, "key mismatch at %d (n=%d, bits [%d,%d))" % (i, keys.size, b, e)
+
+
+@pytest.mark.parametrize("key_type", KEY_TYPES)
+@pytest.mark.parametrize("pairs", [False, True])
+def test_sizes_and_ranges(key_type, pairs):
+    ksz = np.dtype(inputs.KEY_DTYPES[key_type]).itemsize
+    lim = TINY_MAX[(ksz, pairs)]
+    for n in (0, 1, 1000, lim, lim + 1, TILE * 3 - 1, TILE * 3, TILE * 5 + 17, 100_003):
+        for dist in ("uniform", "dup"):
+            keys = inputs.random_keys(key_type, n, 2000 + n, dist)
+            vals = np.arange(n, dtype=np.uint32) if pairs else None
+            for b, e in RANGES[key_type]:
+                announce("digits11 %s pairs=%s n=%d dist=%s bits=[%d,%d)" % (key_type, pairs, n, dist, b, e))
+                _compare(keys, vals, b, e)
+
+
+@pytest.mark.parametrize("key_type,dist", [("u32", "and3"), ("u64", "and3"), ("f32", "f32mix"),
+                                           ("i32", "and3"), ("f64", "fmix"), ("i64", "dup")])
+def test_skewed_and_special_values(key_type, dist):
+    n = 40 * TILE + 1234
+    keys = inputs.random_keys(key_type, n, 78, dist)
+    bits = 8 * keys.dtype.itemsize
+    for pairs in (False, True):
+        vals = np.random.default_rng(6).permutation(n).astype(np.uint32) if pairs else None
+        for b, e in [(0, bits), (3, bits - 2)]:
+            announce("digits11 skew %s %s pairs=%s bits=[%d,%d)" % (key_type, dist, pairs, b, e))
+            _compare(keys, vals, b, e)
+
+
+REDUCED = {"c2_u32_keys_1e8": 4_194_304 + 1237, "c3a_u32_pairs_and3": 2_097_152 + 999,
+           "c4_f32_pairs_normal": 2_097_152 + 77, "c5a_u64_pairs": 1_048_576 + 4095,
+           "c5b_u32_keys_20bit": 2_097_152 + 4097, "f1_f64_pairs_normal": 1_048_576 + 8191}
+
+
+@pytest.mark.parametrize("name", list(REDUCED))
+def test_workloads_reduced_vs_oracle(name):
+    cfg, keys, vals = inputs.draw(name, REDUCED[name])
+    announce("digits11 reduced %s n=%d" % (name, keys.size))
+    _compare(keys, vals, cfg.begin_bit, cfg.end_bit)
+
+
+@pytest.mark.parametrize("key_type,pairs", [("u32", False), ("u32", True), ("f32", False), ("u64", True)])
+def test_block_shapes_vs_oracle(key_type, pairs):
+    """Whole blocks of one to three tiles, and a short last tile, at the
+    number of blocks the chip runs at once (two workgroups per CU for 32-bit
+    keys alone, one otherwise)."""
+    ksz = np.dtype(inputs.KEY_DTYPES[key_type]).itemsize
+    per_cu = 2 if ksz == 4 and not pairs else 1
+    for k in (1, 3):
+        for r in (-1, 1, TILE // 2 + 3):
+            n = CUS * per_cu * k * TILE + r
+            keys = inputs.random_keys(key_type, n, 50 + k, "uniform")
+            vals = np.arange(n, dtype=np.uint32) if pairs else None
+            announce("digits11 block shapes %s pairs=%s n=%d" % (key_type, pairs, n))
+            _compare(keys, vals, 0, 8 * ksz)
+
+
+@pytest.mark.parametrize("key_type", KEY_TYPES)
+def test_in_place(key_type):
+    n = 9 * TILE + 101
+    keys = inputs.random_keys(key_type, n, 19, "fmix" if key_type in ("f32", "f64") else "dup")
+    vals = np.random.default_rng(13).permutation(n).astype(np.uint32)
+    bits = 8 * keys.dtype.itemsize
+    # 1, 2 and 3 passes (odd pass counts in place go through a second alternate buffer)
+    for b, e in [(0, 11), (0, 22), (bits - 32, bits), (4, 9)]:
+        for ipk, ipv in [(True, False), (False, True), (True, True)]:
+            announce("digits11 in-place %s bits=[%d,%d) keys=%s vals=%s" % (key_type, b, e, ipk, ipv))
+            _compare(keys, vals, b, e, in_place_keys=ipk, in_place_vals=ipv)
+        announce("digits11 in-place keys-only %s bits=[%d,%d)" % (key_type, b, e))
+        _compare(keys, None, b, e, in_place_keys=True)
+
+
+def _with_constant_digits(keys, digits):
+    """Keys whose listed 11-bit digits are set to a fixed value (the others random)."""
+    k = keys.view(np.uint32).copy()
+    for d in digits:
+        lo = D * d
+        width = min(D, 32 - lo)
+        m = np.uint32(((1 << width) - 1) << lo)
+        k = (k & ~m) | np.uint32(((0x5A3 ^ d) & ((1 << width) - 1)) << lo)
+    return k
+
+
+@pytest.mark.parametrize("digits", [(0,), (1,), (2,), (0, 1), (1, 2), (0, 2), (0, 1, 2)])
+def test_constant_digit_passes_vs_oracle(digits):
+    """A pass whose 11-bit digit is one value for every key moves nothing."""
+    n = 20 * TILE + 777
+    keys = _with_constant_digits(inputs.random_keys("u32", n, 124, "uniform"), digits)
+    vals = np.random.default_rng(9).permutation(n).astype(np.uint32)
+    for b, e in [(0, 32), (0, 22)]:
+        announce("digits11 constant digits %s bits=[%d,%d)" % (digits, b, e))
+        _compare(keys, vals, b, e)
+        _compare(keys, vals, b, e, in_place_keys=True, in_place_vals=True)
+        _compare(keys, None, b, e)
+
+
+@pytest.mark.parametrize("name", ["c2_u32_keys_1e8", "c3a_u32_pairs_and3", "c4_f32_pairs_normal",
+                                  "c5a_u64_pairs", "f1_i64_pairs"])
+def test_workloads_full_size(name):
+    cfg, keys, vals = inputs.draw(name)
+    announce("digits11 full %s n=%d" % (name, keys.size))
+    got_k, got_v = gpu_sort(keys, vals, cfg.begin_bit, cfg.end_bit, digit_bits=D)
+    if vals is not None:
+        checks.check_pairs(keys, got_k, got_v, cfg.begin_bit, cfg.end_bit)
+    else:
+        i = checks.first_mismatch(got_k, np.sort(keys))
+        assert i < 0, "mismatch with np.sort at %d" % i
+
+
+def test_outputs_past_2gib():
+    """The plain-store form of the 2048-digit downsweep (outputs past a 32-bit
+    byte offset)."""
+    n = (1 << 29) + 12_345
+    keys = inputs.random_keys("u32", n, 12, "dup")
+    vals = np.arange(n, dtype=np.uint32)
+    announce("digits11 wide output u32 pairs n=%d" % n)
+    got_k, got_v = gpu_sort(keys, vals, 0, 32, digit_bits=D)
+    checks.check_pairs(keys, got_k, got_v, 0, 32)
+
+
+def test_generic_call_with_8_bit_digits():
+    """lrs_sort_digits with 8-bit digits runs the typed calls' sort."""
+    for key_type, pairs in [("u32", False), ("f32", True), ("u64", True)]:
+        n = 300_007
+        keys = inputs.random_keys(key_type, n, 21, "uniform")
+        vals = np.arange(n, dtype=np.uint32) if pairs else None
+        bits = 8 * keys.dtype.itemsize
+        announce("generic call, 8-bit digits %s pairs=%s" % (key_type, pairs))
+        a_k, a_v = gpu_sort(keys, vals, 0, bits, digit_bits=8)
+        b_k, b_v = gpu_sort(keys, vals, 0, bits)
+        assert np.array_equal(a_k.view(np.uint8), b_k.view(np.uint8))
+        if pairs:
+            assert np.array_equal(a_v, b_v)
