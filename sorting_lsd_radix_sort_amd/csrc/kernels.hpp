@@ -253,12 +253,30 @@ __device__ __forceinline__ void count_range(const K *__restrict__ keys, int64_t 
             for (int u = 0; u < UNROLL; ++u) {
                 const int64_t i = base + (int64_t)u * THREADS + tid;
                 if (i < vend) {
+                    uint32_t d[PER];
                     if constexpr (sizeof(K) == 4) {
-                        count_key((K)v[u].x); count_key((K)v[u].y);
-                        count_key((K)v[u].z); count_key((K)v[u].w);
+                        d[0] = digit_of<CODE>((K)v[u].x, shift, mask);
+                        d[1] = digit_of<CODE>((K)v[u].y, shift, mask);
+                        d[2] = digit_of<CODE>((K)v[u].z, shift, mask);
+                        d[3] = digit_of<CODE>((K)v[u].w, shift, mask);
                     } else {
-                        count_key((K)(((uint64_t)v[u].y << 32) | v[u].x));
-                        count_key((K)(((uint64_t)v[u].w << 32) | v[u].z));
+                        d[0] = digit_of<CODE>((K)(((uint64_t)v[u].y << 32) | v[u].x), shift, mask);
+                        d[1] = digit_of<CODE>((K)(((uint64_t)v[u].w << 32) | v[u].z), shift, mask);
+                    }
+                    // When every key the wave holds here has one digit (constant
+                    // keys, or a constant digit of this pass), one lane adds them
+                    // all: otherwise 64 lanes would serialize on one LDS word.
+                    const uint32_t f = __builtin_amdgcn_readfirstlane(d[0]);
+                    bool same = true;
+#pragma unroll
+                    for (int k = 0; k < PER; ++k) same = same && d[k] == f;
+                    if (__ballot(!same) == 0) {
+                        const unsigned long long act = __ballot(1);
+                        if ((int)(tid & (kWave - 1)) == __builtin_ffsll((long long)act) - 1)
+                            atomicAdd(&h[f], (uint32_t)(PER * __popcll(act)));
+                    } else {
+#pragma unroll
+                        for (int k = 0; k < PER; ++k) atomicAdd(&h[d[k]], 1u);
                     }
                 }
             }
