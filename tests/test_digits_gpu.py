@@ -154,15 +154,16 @@ def test_workloads_full_size(name):
         assert i < 0, "mismatch with np.sort at %d" % i
 
 
-def test_outputs_past_2gib():
+@pytest.mark.parametrize("key_type,n", [("u32", (1 << 29) + 12_345), ("u64", (1 << 28) + 3)])
+def test_outputs_past_2gib(key_type, n):
     """The plain-store form of the 2048-digit downsweep (outputs past a 32-bit
-    byte offset)."""
-    n = (1 << 29) + 12_345
-    keys = inputs.random_keys("u32", n, 12, "dup")
+    byte offset), checked by the properties that pin the stable sort."""
+    keys = inputs.random_keys(key_type, n, 12, "dup" if key_type == "u32" else "uniform")
     vals = np.arange(n, dtype=np.uint32)
-    announce("digits11 wide output u32 pairs n=%d" % n)
-    got_k, got_v = gpu_sort(keys, vals, 0, 32, digit_bits=D)
-    checks.check_pairs(keys, got_k, got_v, 0, 32)
+    bits = 8 * keys.dtype.itemsize
+    announce("digits11 wide output %s pairs n=%d" % (key_type, n))
+    got_k, got_v = gpu_sort(keys, vals, 0, bits, digit_bits=D)
+    checks.check_pairs(keys, got_k, got_v, 0, bits)
 
 
 def test_generic_call_with_8_bit_digits():
