@@ -46,11 +46,18 @@ def cpu_model() -> str:
 
 
 def kernel_source_digest() -> str:
+    """Digest of the library's source code with comments and blank space
+    removed: a change to the kernels changes it, a change to their comments
+    does not."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for rel in ("sorting_lsd_radix_sort_amd/csrc/kernels.hpp", "sorting_lsd_radix_sort_amd/csrc/lrsort.hip"):
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

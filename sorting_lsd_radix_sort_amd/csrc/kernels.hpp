@@ -397,10 +397,13 @@ __global__ __launch_bounds__(THREADS) void scan_kernel(uint32_t *__restrict__ co
 // one workgroup per CU).
 //
 // Stores are buffer stores (outputs up to 2 GiB): a lane with nothing to store
-// gives an offset past the output buffer, which the buffer's range check drops.
-// No store sits in a branch, every path issues the same memory operations, and
-// the wait for the next tile's loads is counted exactly.  WIDE outputs use
-// plain stores under a branch instead.
+// gives an offset past the output buffer, which the buffer's range check drops,
+// so the carry stores and the register-carry path's stores sit in no branch.
+// With the carry in LDS, a tile key is either stored or written to the carry,
+// and one compare picks the side of an if/else (a select for the store offset
+// cost a second compare and the select itself per key).  The wait for the next
+// tile's loads stays exact: loads are issued on every path.  WIDE outputs use
+// plain stores under a branch.
 
 // Buffer resource over `bytes` bytes from `base`: buffer loads through it at
 // byte offsets at or past `bytes` return zero without touching memory.
@@ -862,7 +865,8 @@ __global__ __launch_bounds__(WAVES *kWave)
                     store_out<true>(xk[i], keys_out, kout_buf, at, !held);
                     if (held) s.carry[digit_of<CODE>(xk[i], shift, mask)][at & (LINE - 1u)] = xk[i];
                 } else {
-                    // byte offset of lane (at / PU) % LINE in the digit's carry row
+                    // stored, or kept at byte offset (lane (at / PU) % LINE) of
+                    // the digit's carry row
                     if (!held)
                         buffer_store<K>(xk[i], kout_buf, at);
                     else
