@@ -741,6 +741,19 @@ __global__ __launch_bounds__(WAVES *kWave)
         }
         __syncthreads();
 
+        // With the carry in LDS: this thread's carry lanes, read now.  The
+        // carry holds what the previous tile left (its writes came before the
+        // barrier above), and every read here precedes the next barrier, after
+        // which this tile's held-back keys overwrite it.
+        K cx[CARRY_LDS ? CARRY : 1];
+        if constexpr (CARRY_LDS) {
+            int tid_c = tid;
+            asm volatile("" : "+v"(tid_c));
+#pragma unroll
+            for (int i = 0; i < CARRY; ++i)
+                cx[i] = s.carry[(uint32_t)i * (THREADS / LINE) + (uint32_t)tid_c / LINE][(uint32_t)tid_c % LINE];
+        }
+
         // Every wave forms the digit offsets itself (4 digits per lane): its
         // own prefix over the waves before it, and the tile's exclusive prefix
         // over digits.  Redundant across waves, but it needs no second barrier
@@ -829,21 +842,12 @@ __global__ __launch_bounds__(WAVES *kWave)
         if constexpr (CARRY_LDS) {
             // Consecutive threads take consecutive lanes of a digit's carry
             // line: a wave stores whole lines.
-            // Reads first, then stores (as for the tile's keys below).
             uint2 pe[CARRY];
-            K cx[CARRY];
 #pragma unroll
-            for (int i = 0; i < CARRY; ++i) {
-                const uint32_t d = (uint32_t)i * (THREADS / LINE) + drow;
-                pe[i] = s.pend[d];
-                cx[i] = s.carry[d][e];
-            }
+            for (int i = 0; i < CARRY; ++i) pe[i] = s.pend[(uint32_t)i * (THREADS / LINE) + drow];
 #pragma unroll
             for (int i = 0; i < CARRY; ++i)
                 store_out<WIDE>(cx[i], keys_out, kout_buf, pe[i].x + e, ((pe[i].y >> e) & 1u) != 0u);
-            // Every carry lane is read before the tile's held-back keys
-            // overwrite the lines that filled.
-            __syncthreads();
             // In phases, so that the LDS reads of all items are in flight
             // together rather than one item's at a time: the keys, then their
             // digits' placements, then the stores.  Keys past their digit's
