@@ -310,17 +310,21 @@ __global__ __launch_bounds__(THREADS) void upsweep_kernel(
     if (col >= num_blocks) return;  // the launch rounds the grid up to kXcds * per
     const K *__restrict__ keys = (const K *)bufs.keys[pass_source(route, pass, src_fixed)];
     constexpr int WAVES = THREADS / kWave;
-    // COPIES sub-histograms per wave (lane % COPIES picks one), padded by one
-    // word so that equal digits in different copies fall in different banks:
-    // skewed digits then serialize at most 64/COPIES lanes per atomic.  With
-    // 2048 digits one copy per wave (64 KB in all) is what LDS holds.
+    // COPIES sub-histograms (lane % COPIES picks one), padded by one word so
+    // that equal digits in different copies fall in different banks: skewed
+    // digits then serialize at most 64/COPIES lanes per atomic.  With 256
+    // digits each wave has its own copies; with 2048 the workgroup's waves
+    // share them (32 KB, against 256 KB for copies per wave), which leaves
+    // room for four workgroups per CU.
     constexpr int RADIX = 1 << RB;
-    constexpr int COPIES = RB == kRadixBits ? 4 : 1;
+    constexpr int COPIES = 4;
+    constexpr bool SHARED = RB != kRadixBits;
+    constexpr int ROWS = SHARED ? COPIES : WAVES * COPIES;
     constexpr int STRIDE = RADIX + 1;
-    __shared__ uint32_t hist[WAVES * COPIES][STRIDE];
+    __shared__ uint32_t hist[ROWS][STRIDE];
     const int tid = threadIdx.x;
-    uint32_t *h = hist[(tid / kWave) * COPIES + (tid % COPIES)];
-    for (int i = tid; i < WAVES * COPIES * STRIDE; i += THREADS) (&hist[0][0])[i] = 0u;
+    uint32_t *h = hist[SHARED ? (tid % COPIES) : (tid / kWave) * COPIES + (tid % COPIES)];
+    for (int i = tid; i < ROWS * STRIDE; i += THREADS) (&hist[0][0])[i] = 0u;
     __syncthreads();
 
     const int64_t begin = (int64_t)col * block_len;
@@ -332,7 +336,7 @@ __global__ __launch_bounds__(THREADS) void upsweep_kernel(
     for (int d = tid; d < RADIX; d += THREADS) {
         uint32_t s = 0;
 #pragma unroll
-        for (int w = 0; w < WAVES * COPIES; ++w) s += hist[w][d];
+        for (int w = 0; w < ROWS; ++w) s += hist[w][d];
         counts[(int64_t)d * num_blocks + col] = s;
     }
 }
