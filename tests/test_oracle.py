@@ -320,6 +320,27 @@ def test_partial_range_composes(key_type):
         assert ko.view(words.dtype).tolist() == back
 
 
+@pytest.mark.parametrize("key_type,widths", [("u32", (11, 11, 10)), ("u32", (8, 8, 8, 8)), ("u32", (3, 16, 13)),
+                                             ("f32", (11, 11, 10)), ("u64", (11,) * 5 + (9,)),
+                                             ("i64", (16, 16, 16, 16)), ("u32", (32,))])
+def test_digit_width_does_not_change_the_result(key_type, widths):
+    """Stable sorts by consecutive bit fields, least significant first, give the
+    stable sort by the whole field whatever the widths: the reading under the
+    11-bit digit option (three passes of 11, 11 and 10 bits for 32-bit keys)."""
+    x = inputs.random_keys(key_type, 3000, 31, "dup" if key_type in ("u32", "i64") else "fmix" if key_type == "f32" else "uniform")
+    pay = np.random.default_rng(8).permutation(x.size).astype(np.uint32)
+    bits = sum(widths)
+    assert bits == 8 * x.dtype.itemsize
+    ko, vo = x, pay
+    b = 0
+    for w in widths:
+        ko, vo = oracle.sort_pairs(ko, vo, b, b + w)
+        b += w
+    want_k, want_v = oracle.sort_pairs(x, pay, 0, bits)
+    assert np.array_equal(vo, want_v)
+    assert np.array_equal(ko.view(np.uint8), want_k.view(np.uint8))
+
+
 # ------------------------------------------------------- library cross-check
 
 @pytest.mark.parametrize("key_type,dist", [("u32", "uniform"), ("u32", "dup"), ("u32", "and3"),
