@@ -32,13 +32,10 @@ namespace {
 
 using namespace lrs;
 
-// Key types: storage width and order code (see order_code in kernels.hpp).
+// Key types; each selects a storage width and an order code (order_code in
+// kernels.hpp) through run_kind's template arguments.
 enum KeyKind { KIND_U32, KIND_I32, KIND_F32, KIND_U64, KIND_I64, KIND_F64 };
 int key_bytes(KeyKind k) { return k == KIND_U64 || k == KIND_I64 || k == KIND_F64 ? 8 : 4; }
-int key_code(KeyKind k)
-{
-    return k == KIND_I32 || k == KIND_I64 ? CODE_SIGNED : k == KIND_F32 || k == KIND_F64 ? CODE_FLOAT : CODE_UNSIGNED;
-}
 
 constexpr int kMaxBlocks = 4096;  // count-matrix width cap (scan: 256 threads x 16)
 constexpr int kWideDigitBits = 11;  // the other digit width lrs_sort_digits takes
