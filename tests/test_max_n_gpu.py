@@ -64,15 +64,19 @@ def _ordered(x):
 def test_largest_n_uint32_keys(digit_bits):
     import torch
     announce("largest n: %d uint32 keys, %d-bit digits" % (N, digit_bits))
-    kin = _draw(N)
-    want = _summary(kin)
-    kout = torch.empty_like(kin)
-    need = lrs.lrs_sort_digits("u32", digit_bits, None, 0, kin, None, kout, None, N, 0, 32)
-    temp = torch.empty(need, dtype=torch.uint8, device="cuda:0")
-    lrs.lrs_sort_digits("u32", digit_bits, temp, need, kin, None, kout, None, N, 0, 32)
-    torch.cuda.synchronize()
-    del temp
-    assert _ordered(kout), "output not ordered"
-    got = _summary(kout)
-    assert torch.equal(got[0], want[0]), "count per top byte differs"
-    assert got[1] == want[1] and got[2] == want[2], "output keys are not a permutation of the input keys"
+    try:
+        kin = _draw(N)
+        want = _summary(kin)
+        kout = torch.empty_like(kin)
+        need = lrs.lrs_sort_digits("u32", digit_bits, None, 0, kin, None, kout, None, N, 0, 32)
+        temp = torch.empty(need, dtype=torch.uint8, device="cuda:0")
+        lrs.lrs_sort_digits("u32", digit_bits, temp, need, kin, None, kout, None, N, 0, 32)
+        torch.cuda.synchronize()
+        del temp
+        assert _ordered(kout), "output not ordered"
+        got = _summary(kout)
+        assert torch.equal(got[0], want[0]), "count per top byte differs"
+        assert got[1] == want[1] and got[2] == want[2], "output keys are not a permutation of the input keys"
+    finally:
+        kin = kout = temp = None
+        torch.cuda.empty_cache()  # 48 GB: not kept from the tests that follow
