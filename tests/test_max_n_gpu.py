@@ -80,3 +80,45 @@ def test_largest_n_uint32_keys(digit_bits):
     finally:
         kin = kout = temp = None
         torch.cuda.empty_cache()  # 48 GB: not kept from the tests that follow
+
+
+def test_uint64_keys_past_2gib():
+    """64-bit keys alone, 2^28 + 5 of them (2 GiB + 40 bytes): the plain-store
+    form of the register-carry downsweep without values, in 8- and 11-bit
+    digits, checked on the device as above (ordered as unsigned words, same
+    count per top byte, sum and hash sum)."""
+    import torch
+    n = (1 << 28) + 5
+    sign = -(1 << 63)
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(21)
+    hi = torch.randint(0, 1 << 32, (n,), dtype=torch.int64, device="cuda:0", generator=g)
+    lo = torch.randint(0, 1 << 32, (n,), dtype=torch.int64, device="cuda:0", generator=g)
+    kin = (hi << 32) | lo
+    del hi, lo
+
+    def summary(x):
+        top = ((x >> 56) & 0xFF)
+        mixed = (x ^ (x >> 29)) * 0x3C79AC492BA7B653  # wraps mod 2^64
+        return torch.bincount(top, minlength=256).cpu(), int((x & 0xFFFFFFFF).sum().item()), \
+            int(((x >> 32) & 0xFFFFFFFF).sum().item()), int((mixed >> 8).sum().item())
+
+    want = summary(kin)
+    for digit_bits in (8, 11):
+        announce("uint64 keys past 2 GiB: n=%d, %d-bit digits" % (n, digit_bits))
+        try:
+            kout = torch.empty_like(kin)
+            need = lrs.lrs_sort_digits("u64", digit_bits, None, 0, kin, None, kout, None, n, 0, 64)
+            temp = torch.empty(need, dtype=torch.uint8, device="cuda:0")
+            lrs.lrs_sort_digits("u64", digit_bits, temp, need, kin, None, kout, None, n, 0, 64)
+            torch.cuda.synchronize()
+            del temp
+            signed = kout ^ sign  # unsigned order as signed order
+            assert bool((signed[1:] >= signed[:-1]).all().item()), "output not ordered"
+            del signed
+            got = summary(kout)
+            assert torch.equal(got[0], want[0]) and got[1:] == want[1:], \
+                "output keys are not a permutation of the input keys"
+        finally:
+            kout = temp = None
+            torch.cuda.empty_cache()
