@@ -1,0 +1,65 @@
+"""The sort captured into a HIP graph (torch.cuda.graph) and replayed.
+
+The library enqueues only kernel launches on the caller's stream (no memset,
+no host synchronization, no allocation), so a sort with its temp storage
+allocated beforehand can be captured.  Each replay runs on new input written
+between replays, with eager work in between, and its output is checked
+against an eager sort of the same input (bit-exact), several times over.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import sorting_lsd_radix_sort_amd as lrs
+from gpu_util import announce, to_dev, to_host
+from sorting_lsd_radix_sort_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("key_type,n,pairs,digit_bits", [("u32", 65_536, False, 8), ("f32", 300_007, True, 8),
+                                                         ("u64", 100_003, True, 8), ("u32", 200_003, False, 11),
+                                                         ("u32", 5_000, True, 8)])
+def test_graph_replays_match_eager(key_type, n, pairs, digit_bits):
+    import torch
+    announce("graph capture %s n=%d pairs=%s digits=%d" % (key_type, n, pairs, digit_bits))
+    first = inputs.random_keys(key_type, n, 90, "fmix" if key_type in ("f32",) else "uniform")
+    kin = to_dev(first)
+    kout = torch.empty_like(kin)
+    vin = to_dev(np.arange(n, dtype=np.uint32)) if pairs else None
+    vout = torch.empty_like(vin) if pairs else None
+    need = lrs.lrs_sort_digits(key_type, digit_bits, None, 0, kin, vin, kout, vout, n, 0,
+                               8 * first.dtype.itemsize)
+    temp = torch.empty(need, dtype=torch.uint8, device="cuda:0")
+    bits = 8 * first.dtype.itemsize
+
+    def sort_on_current_stream():
+        lrs.lrs_sort_digits(key_type, digit_bits, temp, need, kin, vin, kout, vout, n, 0, bits,
+                            torch.cuda.current_stream())
+
+    # eager once (warms the library's per-device caches), then capture
+    sort_on_current_stream()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        sort_on_current_stream()
+    torch.cuda.synchronize()
+
+    for rep in range(4):
+        data = inputs.random_keys(key_type, n, 100 + rep, "dup" if rep % 2 else "uniform")
+        kin.copy_(to_dev(data))
+        if pairs:
+            vin.copy_(to_dev(np.random.default_rng(rep).permutation(n).astype(np.uint32)))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got_k = to_host(kout).copy()
+        got_v = to_host(vout).copy() if pairs else None
+        # eager sort of the same input, with some unrelated eager work first
+        (torch.arange(1 << 20, device="cuda:0") * 3).sum().item()
+        sort_on_current_stream()
+        torch.cuda.synchronize()
+        assert np.array_equal(got_k.view(np.uint8), to_host(kout).view(np.uint8)), "replay %d: keys differ" % rep
+        if pairs:
+            assert np.array_equal(got_v, to_host(vout)), "replay %d: values differ" % rep
