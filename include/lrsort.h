@@ -36,9 +36,14 @@
  *    temp).  With d_temp != NULL, *temp_bytes is the size of d_temp; less than
  *    the requirement gives LRS_ERR_TEMP_TOO_SMALL and nothing is touched.
  *  - All array pointers are device memory owned by the caller.  The library
- *    allocates nothing, keeps no state between calls, and enqueues its kernels
- *    on `stream` asynchronously: results are ready when the stream reaches
- *    them.  d_temp must stay allocated until then.
+ *    allocates nothing and enqueues its kernels on `stream` asynchronously:
+ *    results are ready when the stream reaches them.  d_temp must stay
+ *    allocated until then.  Between calls it keeps only per-device facts it
+ *    looks up once (the CU count, its kernels' occupancy).
+ *  - A call enqueues kernel launches only (no memset, copy engine or host
+ *    synchronization), so a call with its temp storage already allocated can
+ *    be captured into a HIP graph and replayed; the first call on a device is
+ *    best made outside the capture, since it queries the device.
  *  - The input arrays are not modified, except when the caller passes the same
  *    pointer for input and output (in-place sort, same page section 6, third
  *    pitfall), which is allowed for keys and values independently.  Partial
