@@ -63,3 +63,39 @@ def test_graph_replays_match_eager(key_type, n, pairs, digit_bits):
         assert np.array_equal(got_k.view(np.uint8), to_host(kout).view(np.uint8)), "replay %d: keys differ" % rep
         if pairs:
             assert np.array_equal(got_v, to_host(vout)), "replay %d: values differ" % rep
+
+
+def test_concurrent_calls_on_separate_streams():
+    """Calls from several host threads at once, each on its own stream with its
+    own temp storage (the library's per-device caches are shared), each
+    bit-exact with the oracle-checked eager result of its input."""
+    import threading
+    import torch
+    import oracle
+    announce("concurrent calls on separate streams")
+    cases = [("u32", 300_001, 1), ("f32", 200_003, 2), ("u64", 150_001, 3), ("i32", 250_007, 4)]
+    data = {c: inputs.random_keys(c[0], c[1], c[2], "uniform") for c in cases}
+    results, errors = {}, []
+
+    def work(case):
+        try:
+            keys = data[case]
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                kin = to_dev(keys)
+                for _ in range(3):
+                    out = lrs.sort_keys(kin, stream=s)
+            s.synchronize()
+            results[case] = to_host(out)
+        except Exception as e:  # reported below, in the main thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=work, args=(c,)) for c in cases]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for c in cases:
+        want = oracle.sort_keys(data[c])
+        assert np.array_equal(results[c].view(np.uint8), want.view(np.uint8)), c
