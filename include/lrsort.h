@@ -35,6 +35,9 @@
  *    pointers, n and bit range as the real call (in-place use can need more
  *    temp).  With d_temp != NULL, *temp_bytes is the size of d_temp; less than
  *    the requirement gives LRS_ERR_TEMP_TOO_SMALL and nothing is touched.
+ *    d_temp may have any alignment: the library lays its temp out from the
+ *    first 256-byte boundary at or after d_temp, and the size the query
+ *    reports includes 255 bytes for that (an aligned d_temp needs 255 fewer).
  *  - All array pointers are device memory owned by the caller.  The library
  *    allocates nothing and enqueues its kernels on `stream` asynchronously:
  *    results are ready when the stream reaches them.  d_temp must stay

@@ -492,18 +492,21 @@ lrs_status sort_entry(const Request &rq, void *d_temp, size_t *temp_bytes, hipSt
     Request r = rq;
     if (!pairs || rq.n == 0) r.vals_in = nullptr, r.vals_out = nullptr;
     const Layout L = make_layout(r);
+    // d_temp may have any alignment: the layout starts at its first kAlign
+    // boundary, and the size reported covers the worst case of that padding.
     if (d_temp == nullptr) {
-        *temp_bytes = L.total;
+        *temp_bytes = L.total + (kAlign - 1);
         return LRS_OK;
     }
-    if (*temp_bytes < L.total) return LRS_ERR_TEMP_TOO_SMALL;
+    const size_t pad = (kAlign - (uintptr_t)d_temp % kAlign) % kAlign;
+    if (*temp_bytes < L.total + pad) return LRS_ERR_TEMP_TOO_SMALL;
     if (r.n == 0) return LRS_OK;
     if (L.passes == 0) {
         lrs_status st = copy_bytes(r.keys_out, r.keys_in, (size_t)r.n * ksz, stream);
         if (st == LRS_OK && pairs) st = copy_bytes(r.vals_out, r.vals_in, (size_t)r.n * 4, stream);
         return st;
     }
-    char *temp = (char *)d_temp;
+    char *temp = (char *)d_temp + pad;
     switch (r.kind) {
     case KIND_U32: return run_kind<uint32_t, CODE_UNSIGNED>(pairs, r, L, temp, stream);
     case KIND_I32: return run_kind<uint32_t, CODE_SIGNED>(pairs, r, L, temp, stream);

@@ -114,9 +114,13 @@ def test_invalid_sizes_and_pointers():
 
 def test_temp_too_small_and_empty_input_touch_nothing():
     need = q_keys("u32", 1_000_000, 0, 32)
-    with pytest.raises(lrs.LrsError) as ei:
-        lrs.lrs_sort_keys_u32(T, need - 1, A, B, 1_000_000, 0, 32, 0)
-    assert ei.value.status == lrs.LRS_ERR_TEMP_TOO_SMALL
+    # the query covers up to 255 bytes of padding to the first 256-byte
+    # boundary: an aligned temp needs 255 bytes less, a temp one byte past a
+    # boundary needs all of it
+    for t, size in [(T, need - 256), (T + 1, need - 1)]:
+        with pytest.raises(lrs.LrsError) as ei:
+            lrs.lrs_sort_keys_u32(t, size, A, B, 1_000_000, 0, 32, 0)
+        assert ei.value.status == lrs.LRS_ERR_TEMP_TOO_SMALL
     with pytest.raises(lrs.LrsError) as ei:
         lrs.lrs_sort_pairs_f32(T, 16, A, C, B, D, 1_000_000, 0, 32, 0)
     assert ei.value.status == lrs.LRS_ERR_TEMP_TOO_SMALL
@@ -188,6 +192,6 @@ def test_digit_width_argument_checks():
     assert lib.lrs_sort_digits(0, 11, None, None, A, None, B, None, 100, 0, 32, None) == lrs.LRS_ERR_INVALID_ARG
     # a too-small temp is refused before any device work
     need = q_digits("u32", 11, 1_000_000, 0, 32)
-    st = lib.lrs_sort_digits(0, 11, ctypes.c_void_p(T), ctypes.byref(ctypes.c_size_t(need - 1)), A, None, B,
+    st = lib.lrs_sort_digits(0, 11, ctypes.c_void_p(T + 1), ctypes.byref(ctypes.c_size_t(need - 1)), A, None, B,
                              None, 1_000_000, 0, 32, None)
     assert st == lrs.LRS_ERR_TEMP_TOO_SMALL

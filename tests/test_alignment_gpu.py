@@ -1,0 +1,104 @@
+"""Arrays and temp storage that are not 16-byte aligned, on cuda:0.
+
+The boundary requires each array to be aligned to its element size only, and
+accepts temp storage at any address.  Here keys, values, outputs and temp start
+at offsets that break 16-byte (and for temp, any) alignment, each by a
+different amount, and the result is compared element by element with the
+oracle: keys alone and pairs, 32- and 64-bit keys, 8- and 11-bit digits, sizes
+that take the one-workgroup sort, the small-tile and the 16-wave downsweeps,
+out of place and in place.  The inputs must come back untouched.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import sorting_lsd_radix_sort_amd as lrs
+from gpu_util import SFX, announce, to_dev, to_host
+from sorting_lsd_radix_sort_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _slice(a, off):
+    """A device copy of `a` that starts `off` elements into a larger buffer."""
+    import torch
+    base = torch.empty(a.size + off, dtype=to_dev(a[:0]).dtype, device="cuda:0")
+    view = base[off:]
+    view.copy_(to_dev(a))
+    return base, view
+
+
+def _empty_at(like, off):
+    import torch
+    base = torch.empty(like.numel() + off, dtype=like.dtype, device="cuda:0")
+    return base, base[off:]
+
+
+@pytest.mark.parametrize("key_type", ["u32", "f32", "u64", "f64"])
+@pytest.mark.parametrize("pairs", [False, True])
+@pytest.mark.parametrize("digit_bits", [8, 11])
+def test_misaligned_arrays_and_temp(key_type, pairs, digit_bits):
+    import torch
+    ksz = np.dtype(inputs.KEY_DTYPES[key_type]).itemsize
+    bits = 8 * ksz
+    sizes = [3_001, 150_001, 2_500_001 if ksz == 4 else 1_000_003]
+    for n in sizes:
+        keys = inputs.random_keys(key_type, n, 600 + n % 97, "dup" if n % 2 else "uniform")
+        vals = np.random.default_rng(n).permutation(n).astype(np.uint32) if pairs else None
+        # element offsets: 1 for keys in, 3 (32-bit) or 1 (64-bit) for keys out,
+        # 2 and 1 for values in and out; temp one byte past a 256-byte boundary
+        kin_keep, kin = _slice(keys, 1)
+        kout_keep, kout = _empty_at(kin, 3 if ksz == 4 else 1)
+        vin_keep = vin = vout_keep = vout = None
+        if pairs:
+            vin_keep, vin = _slice(vals, 2)
+            vout_keep, vout = _empty_at(vin, 1)
+        assert kin.data_ptr() % 16 and kout.data_ptr() % 16
+        assert not pairs or (vin.data_ptr() % 16 and vout.data_ptr() % 16)
+        need = lrs.lrs_sort_digits(key_type, digit_bits, None, 0, kin, vin, kout, vout, n, 0, bits)
+        temp_keep = torch.empty(need + 1, dtype=torch.uint8, device="cuda:0")
+        temp = temp_keep[1:]
+        announce("misaligned %s pairs=%s digits=%d n=%d" % (key_type, pairs, digit_bits, n))
+        lrs.lrs_sort_digits(key_type, digit_bits, temp, need, kin, vin, kout, vout, n, 0, bits)
+        torch.cuda.synchronize()
+        if pairs:
+            want_k, want_v = oracle.sort_pairs(keys, vals)
+            assert np.array_equal(to_host(vout), want_v), "values differ (n=%d)" % n
+            assert np.array_equal(to_host(vin), vals), "values input changed"
+        else:
+            want_k = oracle.sort_keys(keys)
+        assert np.array_equal(to_host(kout).view(np.uint8), want_k.view(np.uint8)), "keys differ (n=%d)" % n
+        assert np.array_equal(to_host(kin).view(np.uint8), keys.view(np.uint8)), "keys input changed"
+
+
+@pytest.mark.parametrize("key_type,pairs", [("u32", True), ("u64", False), ("f32", False)])
+def test_misaligned_in_place(key_type, pairs):
+    """In place (input and output the same misaligned array), with an odd
+    pass count (three 8-bit passes over 24 bits), which goes through a
+    second alternate buffer, and with four passes."""
+    import torch
+    ksz = np.dtype(inputs.KEY_DTYPES[key_type]).itemsize
+    n = 400_009
+    keys = inputs.random_keys(key_type, n, 41, "uniform")
+    vals = np.arange(n, dtype=np.uint32) if pairs else None
+    for b, e in [(0, 24), (8 * ksz - 32, 8 * ksz)]:
+        _kk, k = _slice(keys, 1)
+        _vk, v = _slice(vals, 3) if pairs else (None, None)
+        fn_name = ("lrs_sort_pairs_" if pairs else "lrs_sort_keys_") + key_type
+        fn = getattr(lrs, fn_name)
+        args = (k, v, k, v) if pairs else (k, k)
+        need = fn(None, 0, *args, n, b, e)
+        temp_keep = torch.empty(need + 8, dtype=torch.uint8, device="cuda:0")
+        temp = temp_keep[8:]
+        announce("misaligned in place %s pairs=%s bits=[%d,%d)" % (key_type, pairs, b, e))
+        fn(temp, need, *args, n, b, e)
+        torch.cuda.synchronize()
+        if pairs:
+            want_k, want_v = oracle.sort_pairs(keys, vals, b, e)
+            assert np.array_equal(to_host(v), want_v)
+        else:
+            want_k = oracle.sort_keys(keys, b, e)
+        assert np.array_equal(to_host(k).view(np.uint8), want_k.view(np.uint8))
+        assert SFX[keys.dtype] == key_type
