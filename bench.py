@@ -86,8 +86,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="c2_u32_keys_1e8")
-    ap.add_argument("--cpu-sample", type=int, default=1 << 25,
-                    help="keys of the input the CPU oracle sorts for the baseline")
+    ap.add_argument("--cpu-sample", type=int, default=0,
+                    help="keys of the input the CPU oracle sorts for the baseline (0: all of them)")
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--digit-bits", type=int, default=8, choices=(8, 11),
@@ -234,15 +234,16 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-        m = min(args.cpu_sample, n)
+        m = min(args.cpu_sample, n) if args.cpu_sample > 0 else n
         sample_k = np.ascontiguousarray(keys_np[:m])
         sample_v = None if vals_np is None else np.arange(m, dtype=np.uint32)
         log("[bench] CPU oracle on %d keys x %d runs" % (m, args.cpu_reps))
         times = oracle.time_sort(sample_k, sample_v, cfg.begin_bit, cfg.end_bit, reps=args.cpu_reps)
         t = statistics.median(times)
         cpu = {"value": m / t / 1e9, "unit": "Gkeys/s", "cores": 1, "kind": "oracle",
-               "sample": "first %d keys of the same input, %s, median of %d runs, one host thread "
-                         "of %d (%s)" % (m, "pairs" if vals_np is not None else "keys only",
+               "sample": "%s %d keys of the same input, %s, median of %d runs, one host thread "
+                         "of %d (%s)" % ("all" if m == n else "first", m,
+                                         "pairs" if vals_np is not None else "keys only",
                                          args.cpu_reps, os.cpu_count() or 0, cpu_model()),
                "seconds": t}
 
