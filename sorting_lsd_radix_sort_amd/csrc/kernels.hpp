@@ -568,8 +568,6 @@ struct DownsweepSmem {
     // for a carry in registers, {tile slot of the line left open after the
     // tile, carry lanes to reload from the tile}.
     alignas(16) std::conditional_t<kCarryLds, uint2, uint4> pend[kRadix];
-    alignas(16) uint32_t run[kRadix];    // next output index of digit d in this block
-    alignas(16) uint32_t start[kRadix];  // first output index of digit d in this block
 };
 
 template <typename K, bool PAIRS, int WAVES, int ITEMS, int CODE, bool WIDE>
@@ -610,20 +608,15 @@ __global__ __launch_bounds__(WAVES *kWave)
     const int vsrc = PAIRS ? pass_source(route_v, pass, vsrc_fixed) : 0;
     const K *__restrict__ keys_in = (const K *)bufs.keys[ksrc];
 
-    // Digit totals (4 digits per lane) and, for wave 0, this block's prefix
-    // within each digit.  The upsweep counted each block as `split`
-    // consecutive sub-blocks (count_cols columns in all): the block's prefix
-    // is the one of its first sub-block.
+    // Digit totals (4 digits per lane) and, for waves 0-3, this block's prefix
+    // within one digit each: wave k owns digit 4*lane + k in the run
+    // placement below.  The upsweep counted each block as `split` consecutive
+    // sub-blocks (count_cols columns in all): the block's prefix is the one of
+    // its first sub-block.
     const uint4 tot4 = reinterpret_cast<const uint4 *>(row_total)[lane];
-    uint4 before4 = make_uint4(0u, 0u, 0u, 0u);
-    if (wave == 0) {
-        const int d0 = 4 * lane;
-        const int64_t col = (int64_t)blk * split;
-        before4.x = counts[(int64_t)(d0 + 0) * count_cols + col];
-        before4.y = counts[(int64_t)(d0 + 1) * count_cols + col];
-        before4.z = counts[(int64_t)(d0 + 2) * count_cols + col];
-        before4.w = counts[(int64_t)(d0 + 3) * count_cols + col];
-    }
+    uint32_t before_own = 0u;
+    if (wave < 4)
+        before_own = counts[(int64_t)(4 * lane + wave) * count_cols + (int64_t)blk * split];
 
     // The pass is skipped when one digit holds every key (every wave tests the
     // totals itself, so the decision is uniform without a barrier).
@@ -639,15 +632,15 @@ __global__ __launch_bounds__(WAVES *kWave)
     const uint32_t *__restrict__ vals_in = PAIRS ? bufs.vals[vsrc] : nullptr;
     uint32_t *__restrict__ vals_out = PAIRS ? (uint32_t *)bufs.vals[vdst] : nullptr;
 
-    // The block's first output index of each digit (digit start plus the
-    // block's prefix); waves 0-3 read and advance these, each its own digits.
-    if (wave == 0) {
-        const uint4 start = wave_scan_digits(tot4);
-        const uint4 first =
-            make_uint4(start.x + before4.x, start.y + before4.y, start.z + before4.z, start.w + before4.w);
-        reinterpret_cast<uint4 *>(s.run)[lane] = first;
-        reinterpret_cast<uint4 *>(s.start)[lane] = first;
+    // The block's first output index of its own digit (digit start plus the
+    // block's prefix) and the next output index of that digit, in registers
+    // of waves 0-3.
+    uint32_t start_own = 0u;
+    if (wave < 4) {
+        const uint4 st = wave_scan_digits(tot4);
+        start_own = (wave == 0 ? st.x : wave == 1 ? st.y : wave == 2 ? st.z : st.w) + before_own;
     }
+    uint32_t run_own = start_own;
 
     // Makes the compiler wait here for a buffer's loads.
     auto ready = [](K(&kb)[ITEMS]) {
@@ -812,14 +805,14 @@ __global__ __launch_bounds__(WAVES *kWave)
             // The padding slots of a short last tile were counted under digit
             // `mask`; they sit after that digit's real keys and are never
             // stored.
-            const uint32_t lo = s.run[d];
+            const uint32_t lo = run_own;
             const uint32_t hi = lo + tt - (d == mask ? (uint32_t)(TILE - valid) : 0u);
             const uint32_t base = lo - of;               // output index of tile slot 0 of the digit
             const uint32_t open = lo & ~(LINE - 1u);     // line holding the carry
             const uint32_t next = hi & ~(LINE - 1u);     // line left open after this tile
             // Carry lanes before the block's first index belong to the
             // previous block.
-            const uint32_t first_idx = s.start[d];
+            const uint32_t first_idx = start_own;
             const uint32_t mine = first_idx > open ? first_idx - open : 0u;
             // The carry goes out when its line fills, or at the block's end
             // (never past n: only a key array changed under a running sort
@@ -834,7 +827,7 @@ __global__ __launch_bounds__(WAVES *kWave)
                 s.pend[d] = make_uint2(open, bit_range(mine, put_to));
             else
                 s.pend[d] = make_uint4(open, bit_range(mine, put_to), next - base, bit_range(keep, fill));
-            s.run[d] = hi;
+            run_own = hi;
         }
         __syncthreads();
 
