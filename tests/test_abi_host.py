@@ -195,3 +195,15 @@ def test_digit_width_argument_checks():
     st = lib.lrs_sort_digits(0, 11, ctypes.c_void_p(T + 1), ctypes.byref(ctypes.c_size_t(need - 1)), A, None, B,
                              None, 1_000_000, 0, 32, None)
     assert st == lrs.LRS_ERR_TEMP_TOO_SMALL
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    """Without the built HIP library the binding raises; there is no other path."""
+    monkeypatch.setattr(lrs, "_lib", None)
+    monkeypatch.setattr(lrs, "LIB_PATH", os.path.join(ROOT, "no_such_dir", "liblrsort.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        lrs.load_library()
+    with pytest.raises(RuntimeError, match="not built"):
+        lrs.lrs_sort_keys_u32(None, 0, A, B, 10, 0, 32)
+    with pytest.raises(RuntimeError, match="not built"):
+        lrs.lrs_sort_digits("u32", 11, None, 0, A, None, B, None, 10, 0, 32)
