@@ -84,7 +84,8 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=50,
+                    help="untimed sorts before the timed ones (the first few dozen after an idle spell run slower)")
     ap.add_argument("--config", default="c2_u32_keys_1e8")
     ap.add_argument("--cpu-sample", type=int, default=0,
                     help="keys of the input the CPU oracle sorts for the baseline (0: all of them)")
