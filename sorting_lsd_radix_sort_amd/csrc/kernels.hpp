@@ -228,11 +228,33 @@ __device__ __forceinline__ int pass_dest(int src, int planned, bool last, bool s
 // Adds the digits of keys [begin, end) into the LDS histogram h (atomics),
 // THREADS lanes striding together.  16-byte loads, UNROLL in flight per lane,
 // where the array and `begin` are 16-byte aligned; single keys otherwise.
-template <typename K, int CODE, int THREADS, int UNROLL = 4>
+// With SPREAD, it also folds the keys into code_and and code_or, from which
+// the bits that differ between the keys' order codes follow (AND xor OR).
+// Unsigned and signed codes differ from the key bits by a fixed xor, which
+// leaves those bits unchanged, so only float keys are folded as codes.
+template <typename K, int CODE, int THREADS, bool SPREAD = false, int UNROLL = 4>
 __device__ __forceinline__ void count_range(const K *__restrict__ keys, int64_t begin, int64_t end,
-                                            uint32_t *h, int tid, int shift, uint32_t mask)
+                                            uint32_t *h, int tid, int shift, uint32_t mask, K &code_and,
+                                            K &code_or)
 {
-    auto count_key = [&](K k) { atomicAdd(&h[digit_of<CODE>(k, shift, mask)], 1u); };
+    auto fold = [](K k) { return CODE == CODE_FLOAT ? order_code<K, CODE>(k) : k; };
+    auto spread = [&](K k) {
+        if constexpr (SPREAD) {
+            code_and &= fold(k);
+            code_or |= fold(k);
+        }
+    };
+    // four keys at once: three-input AND and OR
+    auto spread4 = [&](K a, K b, K c, K d) {
+        if constexpr (SPREAD) {
+            code_and = code_and & fold(a) & fold(b) & (fold(c) & fold(d));
+            code_or = code_or | fold(a) | fold(b) | (fold(c) | fold(d));
+        }
+    };
+    auto count_key = [&](K k) {
+        spread(k);
+        atomicAdd(&h[digit_of<CODE>(k, shift, mask)], 1u);
+    };
     constexpr int PER = 16 / (int)sizeof(K);
     int64_t scalar_from = begin;
     if ((((uintptr_t)keys & 15) == 0) && begin % PER == 0) {
@@ -255,11 +277,14 @@ __device__ __forceinline__ void count_range(const K *__restrict__ keys, int64_t 
                 if (i < vend) {
                     uint32_t d[PER];
                     if constexpr (sizeof(K) == 4) {
+                        spread4((K)v[u].x, (K)v[u].y, (K)v[u].z, (K)v[u].w);
                         d[0] = digit_of<CODE>((K)v[u].x, shift, mask);
                         d[1] = digit_of<CODE>((K)v[u].y, shift, mask);
                         d[2] = digit_of<CODE>((K)v[u].z, shift, mask);
                         d[3] = digit_of<CODE>((K)v[u].w, shift, mask);
                     } else {
+                        spread((K)(((uint64_t)v[u].y << 32) | v[u].x));
+                        spread((K)(((uint64_t)v[u].w << 32) | v[u].z));
                         d[0] = digit_of<CODE>((K)(((uint64_t)v[u].y << 32) | v[u].x), shift, mask);
                         d[1] = digit_of<CODE>((K)(((uint64_t)v[u].w << 32) | v[u].z), shift, mask);
                     }
@@ -293,10 +318,21 @@ __device__ __forceinline__ void count_range(const K *__restrict__ keys, int64_t 
 // section 8.1: per-block and per-warp counting instead of global atomics).
 // The keys are read 16 bytes per lane when their array is 16-byte aligned.
 // RB is the digit width: 8, or 11 for the 2048-digit passes.
-template <typename K, int CODE, int THREADS, int RB = kRadixBits>
+// Bits that differ between the order codes of a sort's keys (their AND xor
+// their OR) show which passes have a constant digit: the first pass records
+// the AND and OR of each column (SPREAD), the first scan combines them, and a
+// later pass whose digit bits are all equal there returns at once in every
+// kernel (no key is read; its downsweep leaves the data where it is).
+__device__ __forceinline__ bool digit_constant(const unsigned long long *diff, int shift, uint32_t mask)
+{
+    return ((*diff >> shift) & (unsigned long long)mask) == 0ull;
+}
+
+template <typename K, int CODE, int THREADS, int RB = kRadixBits, bool SPREAD = false>
 __global__ __launch_bounds__(THREADS) void upsweep_kernel(
     SortBufs bufs, const uint32_t *__restrict__ route, int pass, int src_fixed, uint32_t *__restrict__ counts,
-    int64_t n, int64_t block_len, int num_blocks, int shift, uint32_t mask)
+    int64_t n, int64_t block_len, int num_blocks, int shift, uint32_t mask,
+    unsigned long long *__restrict__ spread_out, const unsigned long long *__restrict__ diff_in)
 {
     // The count matrix is digit-major, so a workgroup's 256 counts land in 256
     // different rows, 4 bytes in each 128-byte line.  Workgroups go to the
@@ -326,12 +362,35 @@ __global__ __launch_bounds__(THREADS) void upsweep_kernel(
     uint32_t *h = hist[SHARED ? (tid % COPIES) : (tid / kWave) * COPIES + (tid % COPIES)];
     for (int i = tid; i < ROWS * STRIDE; i += THREADS) (&hist[0][0])[i] = 0u;
     __syncthreads();
+    // (tested after the histograms are cleared, so the two latencies overlap)
+    if (diff_in != nullptr && digit_constant(diff_in, shift, mask)) return;
 
     const int64_t begin = (int64_t)col * block_len;
     const int64_t end = begin + block_len < n ? begin + block_len : n;
 
-    count_range<K, CODE, THREADS>(keys, begin, end, h, tid, shift, mask);
+    K code_and = ~(K)0, code_or = (K)0;
+    count_range<K, CODE, THREADS, SPREAD>(keys, begin, end, h, tid, shift, mask, code_and, code_or);
+    __shared__ unsigned long long wave_spread[SPREAD ? WAVES : 1][2];
+    if constexpr (SPREAD) {
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            code_and &= __shfl_xor(code_and, o);
+            code_or |= __shfl_xor(code_or, o);
+        }
+        if ((tid & (kWave - 1)) == 0) {
+            wave_spread[tid / kWave][0] = (unsigned long long)code_and;
+            wave_spread[tid / kWave][1] = (unsigned long long)code_or;
+        }
+    }
     __syncthreads();
+    if constexpr (SPREAD) {
+        if (tid == 0) {
+            unsigned long long a = ~0ull, o = 0ull;
+            for (int w = 0; w < WAVES; ++w) a &= wave_spread[w][0], o |= wave_spread[w][1];
+            spread_out[2 * col] = a;
+            spread_out[2 * col + 1] = o;
+        }
+    }
 
     for (int d = tid; d < RADIX; d += THREADS) {
         uint32_t s = 0;
@@ -347,22 +406,49 @@ __global__ __launch_bounds__(THREADS) void upsweep_kernel(
 // exclusive prefix sums in place; row_total[d] gets the row's sum.  One
 // workgroup per digit.  The digit starts (exclusive prefix of row_total) are
 // formed by each downsweep workgroup from the 256 totals.
+//
+// The first scan of a sort that recorded its codes' spread (spread_cols, one
+// AND and one OR per column) also combines them, in workgroup 0, into
+// *diff_out; a later scan returns at once when its digit is constant.
 template <int THREADS, int MAX_PER_THREAD>
 __global__ __launch_bounds__(THREADS) void scan_kernel(uint32_t *__restrict__ counts,
-                                                       uint32_t *__restrict__ row_total, int num_blocks)
+                                                       uint32_t *__restrict__ row_total, int num_blocks,
+                                                       const unsigned long long *__restrict__ spread_cols,
+                                                       unsigned long long *__restrict__ diff_out,
+                                                       const unsigned long long *__restrict__ diff_in, int shift,
+                                                       uint32_t mask)
 {
+    if (spread_cols != nullptr && blockIdx.x == 0) {
+        __shared__ unsigned long long s_spread[THREADS / kWave][2];
+        unsigned long long a = ~0ull, o = 0ull;
+        for (int c = threadIdx.x; c < num_blocks; c += THREADS) a &= spread_cols[2 * c], o |= spread_cols[2 * c + 1];
+#pragma unroll
+        for (int x = 1; x < kWave; x <<= 1) {
+            a &= __shfl_xor(a, x);
+            o |= __shfl_xor(o, x);
+        }
+        if ((threadIdx.x & (kWave - 1)) == 0) s_spread[threadIdx.x / kWave][0] = a, s_spread[threadIdx.x / kWave][1] = o;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            for (int w = 1; w < THREADS / kWave; ++w) a &= s_spread[w][0], o |= s_spread[w][1];
+            *diff_out = a ^ o;
+        }
+    }
     __shared__ uint32_t s_tmp[THREADS / kWave];
     uint32_t *row = counts + (int64_t)blockIdx.x * num_blocks;
     const int per = (num_blocks + THREADS - 1) / THREADS;
     const int first = threadIdx.x * per;
     uint32_t v[MAX_PER_THREAD];
-    uint32_t sum = 0;
 #pragma unroll
     for (int i = 0; i < MAX_PER_THREAD; ++i) {
         const int idx = first + i;
         v[i] = (i < per && idx < num_blocks) ? row[idx] : 0u;
-        sum += v[i];
     }
+    // (tested after the row's loads are issued, so the two latencies overlap)
+    if (diff_in != nullptr && digit_constant(diff_in, shift, mask)) return;
+    uint32_t sum = 0;
+#pragma unroll
+    for (int i = 0; i < MAX_PER_THREAD; ++i) sum += v[i];
     uint32_t total;
     uint32_t run = block_exclusive_scan<THREADS>(sum, s_tmp, total);
 #pragma unroll
@@ -576,7 +662,7 @@ __global__ __launch_bounds__(WAVES *kWave)
         SortBufs bufs, uint32_t *__restrict__ route_k, uint32_t *__restrict__ route_v, int pass, int ksrc_fixed,
         int vsrc_fixed, int kplanned, int vplanned, int last, const uint32_t *__restrict__ counts,
         const uint32_t *__restrict__ row_total, int64_t n, int64_t block_len, int count_cols, int split, int shift,
-        uint32_t mask)
+        uint32_t mask, const unsigned long long *__restrict__ diff_in)
 {
     using Smem = DownsweepSmem<K, PAIRS, WAVES, ITEMS>;
     constexpr int THREADS = Smem::kThreads;
@@ -619,8 +705,12 @@ __global__ __launch_bounds__(WAVES *kWave)
         before_own = counts[(int64_t)(4 * lane + wave) * count_cols + (int64_t)blk * split];
 
     // The pass is skipped when one digit holds every key (every wave tests the
-    // totals itself, so the decision is uniform without a barrier).
-    const bool skip = __ballot(tot4.x == n32 || tot4.y == n32 || tot4.z == n32 || tot4.w == n32) != 0;
+    // totals itself, so the decision is uniform without a barrier); after the
+    // first pass, from the codes' spread (this pass's counts were then never
+    // taken).
+    const bool skip = diff_in != nullptr
+                          ? digit_constant(diff_in, shift, mask)
+                          : __ballot(tot4.x == n32 || tot4.y == n32 || tot4.z == n32 || tot4.w == n32) != 0;
     const int kdst = pass_dest(ksrc, kplanned, last != 0, skip);
     const int vdst = PAIRS ? pass_dest(vsrc, vplanned, last != 0, skip) : 0;
     if (blk == 0 && tid == 0) {
@@ -995,7 +1085,7 @@ __global__ __launch_bounds__(kWideDigitWaves *kWave)
         SortBufs bufs, uint32_t *__restrict__ route_k, uint32_t *__restrict__ route_v, int pass, int ksrc_fixed,
         int vsrc_fixed, int kplanned, int vplanned, int last, const uint32_t *__restrict__ counts,
         const uint32_t *__restrict__ row_total, int64_t n, int64_t block_len, int count_cols, int split, int shift,
-        uint32_t mask)
+        uint32_t mask, const unsigned long long *__restrict__ diff_in)
 {
     using Smem = WideDigitSmem<K, PAIRS, RB>;
     constexpr int RADIX = Smem::kRadixW;
@@ -1028,9 +1118,11 @@ __global__ __launch_bounds__(kWideDigitWaves *kWave)
 #pragma unroll
         for (int k = 0; k < 4; ++k) run[k] = counts[(int64_t)(4 * tid + k) * count_cols + col];
     }
-    // The pass is skipped when one digit holds every key.
-    const bool skip =
-        __syncthreads_or(tot4.x == n32 || tot4.y == n32 || tot4.z == n32 || tot4.w == n32) != 0;
+    // The pass is skipped when one digit holds every key (after the first
+    // pass, as the codes' spread shows: this pass's counts were never taken).
+    const bool skip = diff_in != nullptr
+                          ? digit_constant(diff_in, shift, mask)
+                          : __syncthreads_or(tot4.x == n32 || tot4.y == n32 || tot4.z == n32 || tot4.w == n32) != 0;
     const int kdst = pass_dest(ksrc, kplanned, last != 0, skip);
     const int vdst = PAIRS ? pass_dest(vsrc, vplanned, last != 0, skip) : 0;
     if (blk == 0 && tid == 0) {

@@ -211,7 +211,8 @@ struct Layout {
     int64_t tiles = 0;
     int max_cols = 0;  // count-matrix columns (upsweep sub-blocks) at most
     Plan kplan, vplan;
-    size_t off_counts = 0, off_rowtot = 0, off_route = 0, off_ka = 0, off_kb = 0, off_va = 0, off_vb = 0;
+    size_t off_counts = 0, off_rowtot = 0, off_route = 0, off_spread = 0, off_diff = 0, off_ka = 0, off_kb = 0,
+           off_va = 0, off_vb = 0;
     size_t total = 0;
 };
 
@@ -234,6 +235,10 @@ Layout make_layout(const Request &rq)
     off += align_up(radix * 4);
     L.off_route = off;  // where keys, then values, are before each pass and at the end
     off += align_up((size_t)2 * kMaxRoute * 4);
+    L.off_spread = off;  // AND and OR of the order codes, per column of the first pass
+    off += align_up((size_t)2 * L.max_cols * 8);
+    L.off_diff = off;  // their combination over all columns
+    off += align_up(8);
     const size_t kbytes = align_up((size_t)rq.n * ksz), vbytes = align_up((size_t)rq.n * 4);
     if (L.kplan.need_a) { L.off_ka = off; off += kbytes; }
     if (L.kplan.need_b) { L.off_kb = off; off += kbytes; }
@@ -278,22 +283,38 @@ lrs_status copy_bytes(void *dst, const void *src, size_t bytes, hipStream_t stre
 
 // ------------------------------------------------------------ pass launchers
 
+// The codes' spread: where the first pass records it (spread_out, AND and OR
+// per column, and diff_out, their combination) and where later passes read
+// the combination (diff_in); each null where it does not apply.
+struct SpreadArgs {
+    unsigned long long *spread_out = nullptr;
+    unsigned long long *diff_out = nullptr;
+    const unsigned long long *diff_in = nullptr;
+};
+
 template <typename K, int CODE, int RB>
 hipError_t launch_upsweep(const SortBufs &bufs, const uint32_t *route, int pass, int src_fixed, uint32_t *counts,
-                          int64_t n, int64_t block_len, int blocks, int shift, uint32_t mask, hipStream_t stream)
+                          int64_t n, int64_t block_len, int blocks, int shift, uint32_t mask, const SpreadArgs &sp,
+                          hipStream_t stream)
 {
     return launch(LRS_KERNEL_UPSWEEP, stream, [&] {
         const int grid = (blocks + kXcds - 1) / kXcds * kXcds;  // see upsweep_kernel's column mapping
-        upsweep_kernel<K, CODE, kUpsweepThreads, RB><<<grid, kUpsweepThreads, 0, stream>>>(
-            bufs, route, pass, src_fixed, counts, n, block_len, blocks, shift, mask);
+        if (sp.spread_out != nullptr)
+            upsweep_kernel<K, CODE, kUpsweepThreads, RB, true><<<grid, kUpsweepThreads, 0, stream>>>(
+                bufs, route, pass, src_fixed, counts, n, block_len, blocks, shift, mask, sp.spread_out, sp.diff_in);
+        else
+            upsweep_kernel<K, CODE, kUpsweepThreads, RB, false><<<grid, kUpsweepThreads, 0, stream>>>(
+                bufs, route, pass, src_fixed, counts, n, block_len, blocks, shift, mask, nullptr, sp.diff_in);
     });
 }
 
 // One workgroup per digit (row of the count matrix).
-hipError_t launch_scan(uint32_t *counts, uint32_t *rowtot, int blocks, int radix, hipStream_t stream)
+hipError_t launch_scan(uint32_t *counts, uint32_t *rowtot, int blocks, int radix, int shift, uint32_t mask,
+                       const SpreadArgs &sp, hipStream_t stream)
 {
     return launch(LRS_KERNEL_SCAN, stream, [&] {
-        scan_kernel<kScanThreads, kScanPerThread><<<radix, kScanThreads, 0, stream>>>(counts, rowtot, blocks);
+        scan_kernel<kScanThreads, kScanPerThread><<<radix, kScanThreads, 0, stream>>>(
+            counts, rowtot, blocks, sp.spread_out, sp.diff_out, sp.diff_in, shift, mask);
     });
 }
 
@@ -330,12 +351,13 @@ struct PassRoute {
 template <typename K, bool PAIRS, int WAVES, int ITEMS, int CODE, int RB>
 hipError_t launch_downsweep(const SortBufs &bufs, uint32_t *route_k, uint32_t *route_v, const PassRoute &pr,
                             const uint32_t *counts, const uint32_t *rowtot, int64_t n, int64_t block_len,
-                            int blocks, int cols, int split, int shift, uint32_t mask, hipStream_t stream)
+                            int blocks, int cols, int split, int shift, uint32_t mask,
+                            const unsigned long long *diff_in, hipStream_t stream)
 {
     return launch(LRS_KERNEL_DOWNSWEEP, stream, [&] {
         downsweep_fn<K, PAIRS, WAVES, ITEMS, CODE, RB>(wide_output<K>(n))<<<blocks, WAVES * 64, 0, stream>>>(
             bufs, route_k, route_v, pr.pass, pr.ksrc_fixed, pr.vsrc_fixed, pr.kplanned, pr.vplanned, pr.last,
-            counts, rowtot, n, block_len, cols, split, shift, mask);
+            counts, rowtot, n, block_len, cols, split, shift, mask, diff_in);
     });
 }
 
@@ -404,6 +426,8 @@ lrs_status run_passes(const Request &rq, const Layout &L, char *temp, hipStream_
     uint32_t *rowtot = (uint32_t *)(temp + L.off_rowtot);
     uint32_t *route_k = (uint32_t *)(temp + L.off_route);
     uint32_t *route_v = route_k + kMaxRoute;
+    unsigned long long *spread = (unsigned long long *)(temp + L.off_spread);
+    unsigned long long *diff = (unsigned long long *)(temp + L.off_diff);
     const SortBufs bufs = sort_bufs<PAIRS>(rq, L, temp);
     // An in-place array starts in the output buffer (the same memory).
     const int kstart = rq.keys_in == rq.keys_out ? BUF_OUT : BUF_IN;
@@ -421,12 +445,24 @@ lrs_status run_passes(const Request &rq, const Layout &L, char *temp, hipStream_
         pr.vplanned = L.vplan.dst[p];
         pr.last = p == L.passes - 1;
 
+        // With more than one pass, the first records the codes' spread and the
+        // later ones skip all their work when it shows their digit constant.
+        SpreadArgs sp;
+        if (L.passes > 1) {
+            if (p == 0) {
+                sp.spread_out = spread;
+                sp.diff_out = diff;
+            } else {
+                sp.diff_in = diff;
+            }
+        }
         hipError_t err = launch_upsweep<K, CODE, RB>(bufs, route_k, p, pr.ksrc_fixed, counts, rq.n, sub_len, cols,
-                                                     shift, mask, stream);
+                                                     shift, mask, sp, stream);
         if (err != hipSuccess) return LRS_ERR_HIP;
-        if (launch_scan(counts, rowtot, cols, 1 << RB, stream) != hipSuccess) return LRS_ERR_HIP;
+        if (launch_scan(counts, rowtot, cols, 1 << RB, shift, mask, sp, stream) != hipSuccess) return LRS_ERR_HIP;
         err = launch_downsweep<K, PAIRS, WAVES, ITEMS, CODE, RB>(bufs, route_k, route_v, pr, counts, rowtot, rq.n,
-                                                                 block_len, blocks, cols, split, shift, mask, stream);
+                                                                 block_len, blocks, cols, split, shift, mask,
+                                                                 sp.diff_in, stream);
         if (err != hipSuccess) return LRS_ERR_HIP;
     }
     // The data is in the output unless skipped passes left it elsewhere (or a

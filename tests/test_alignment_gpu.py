@@ -102,3 +102,40 @@ def test_misaligned_in_place(key_type, pairs):
             want_k = oracle.sort_keys(keys, b, e)
         assert np.array_equal(to_host(k).view(np.uint8), want_k.view(np.uint8))
         assert SFX[keys.dtype] == key_type
+
+
+@pytest.mark.parametrize("key_type", ["u32", "u64"])
+def test_misaligned_input_with_constant_digits(key_type):
+    """A misaligned key array is counted one key per load in the first pass,
+    which also records the keys' spread; later passes over a constant digit
+    are then skipped.  Constant middle and top digits, pairs and keys alone."""
+    import torch
+    ksz = np.dtype(inputs.KEY_DTYPES[key_type]).itemsize
+    bits = 8 * ksz
+    udt = np.uint32 if ksz == 4 else np.uint64
+    n = 600_011
+    raw = inputs.random_keys(key_type, n, 77, "uniform").view(udt).copy()
+    const = udt(0x5A) << udt(8)                    # digit 1 constant
+    top = udt(0x3C) << udt(bits - 8)               # top digit constant
+    raw = (raw & ~(udt(0xFF) << udt(8)) & ~(udt(0xFF) << udt(bits - 8))) | const | top
+    keys = raw.view(inputs.KEY_DTYPES[key_type])
+    for pairs in (False, True):
+        vals = np.random.default_rng(3).permutation(n).astype(np.uint32) if pairs else None
+        _k, kin = _slice(keys, 1)
+        _o, kout = _empty_at(kin, 1)
+        vin = vout = None
+        if pairs:
+            _v, vin = _slice(vals, 1)
+            _w, vout = _empty_at(vin, 1)
+        for digit_bits in (8, 11):
+            need = lrs.lrs_sort_digits(key_type, digit_bits, None, 0, kin, vin, kout, vout, n, 0, bits)
+            temp = torch.empty(need, dtype=torch.uint8, device="cuda:0")
+            announce("misaligned, constant digits %s pairs=%s digits=%d" % (key_type, pairs, digit_bits))
+            lrs.lrs_sort_digits(key_type, digit_bits, temp, need, kin, vin, kout, vout, n, 0, bits)
+            torch.cuda.synchronize()
+            if pairs:
+                want_k, want_v = oracle.sort_pairs(keys, vals)
+                assert np.array_equal(to_host(vout), want_v)
+            else:
+                want_k = oracle.sort_keys(keys)
+            assert np.array_equal(to_host(kout).view(np.uint8), want_k.view(np.uint8))
