@@ -32,7 +32,7 @@ KEY_TYPE_CODES = {"u32": 0, "i32": 1, "f32": 2, "u64": 3, "i64": 4, "f64": 5}
 DIGIT_BITS = (8, 11)
 EXPORTED = SORT_FUNCTIONS + ("lrs_sort_digits", "lrs_status_string", "lrs_device_copy", "lrs_prof_start",
                              "lrs_prof_stop", "lrs_prof_count", "lrs_prof_read",
-                             "lrs_prof_release")
+                             "lrs_prof_release", "lrs_bench_read")
 
 
 class LrsError(RuntimeError):
@@ -78,6 +78,8 @@ def load_library() -> ctypes.CDLL:
     lib.lrs_prof_read.restype = ci
     lib.lrs_prof_release.argtypes = []
     lib.lrs_prof_release.restype = ci
+    lib.lrs_bench_read.argtypes = [vp, sz, vp, vp]
+    lib.lrs_bench_read.restype = ci
     _lib = lib
     return lib
 
@@ -210,6 +212,11 @@ def lrs_prof_release() -> None:
     load_library().lrs_prof_release()
 
 
+def lrs_bench_read(d_src, nbytes: int, d_result, stream=None) -> None:
+    _check(load_library().lrs_bench_read(_ptr(d_src), int(nbytes), _ptr(d_result), _stream(stream)),
+           "lrs_bench_read")
+
+
 # ------------------------------------------------------------- conveniences
 
 _KEY_SUFFIX = {"torch.uint32": "u32", "torch.int32": "i32", "torch.float32": "f32",
@@ -232,57 +239,116 @@ def _temp_tensor(nbytes, device, temp):
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
+def _side_stream(stream):
+    """The torch stream a call is enqueued on when that is not torch's current
+    stream (None otherwise): tensors the conveniences allocate, or copy into
+    contiguous form, on the current stream are then recorded on it, so that
+    the caching allocator does not hand their memory to other work while the
+    sort still uses it."""
+    import torch
+    if stream is None:
+        return None
+    cur = torch.cuda.current_stream()
+    handle = stream if isinstance(stream, int) else stream.cuda_stream
+    if handle == cur.cuda_stream:
+        return None
+    return stream if not isinstance(stream, int) else torch.cuda.ExternalStream(handle)
+
+
+def _keep_for(side, *tensors):
+    if side is None:
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(side)
+
+
+def _check_out(name, t, n, dtype, device):
+    """An output tensor must be contiguous with n elements of `dtype` on the
+    input's device (checked before anything is enqueued)."""
+    if t.dtype != dtype:
+        raise ValueError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if t.numel() != n:
+        raise ValueError("%s holds %d elements, expected %d" % (name, t.numel(), n))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if t.device != device:
+        raise ValueError("%s is on %s, the input on %s" % (name, t.device, device))
+
+
 def sort_keys(keys, begin_bit: int = 0, end_bit: int | None = None, out=None, temp=None, stream=None,
               digit_bits: int = 8):
-    """Stable ascending sort of a 1-D device tensor of keys (uint32, int32,
+    """Stable ascending sort of a device tensor of keys (uint32, int32,
     float32, uint64, int64 or float64) over bits [begin_bit, end_bit) of their
     order code, in passes of `digit_bits` (8 or 11) bits; returns the output
-    tensor."""
+    tensor.  A tensor of any shape is sorted as the flat array of its elements;
+    `out`, when given, must be contiguous with as many elements, of the same
+    dtype, on the same device (ValueError otherwise, before any work)."""
     import torch
     sfx = key_suffix(keys.dtype)
     end_bit = KEY_BITS[sfx] if end_bit is None else end_bit
+    src = keys
     keys = keys.contiguous()
+    n = keys.numel()
     if out is None:
         out = torch.empty_like(keys)
+    else:
+        _check_out("out", out, n, keys.dtype, keys.device)
+    side = _side_stream(stream)
     if digit_bits != 8:
-        n = keys.numel()
         need = lrs_sort_digits(sfx, digit_bits, None, 0, keys, None, out, None, n, begin_bit, end_bit)
         t = _temp_tensor(need, keys.device, temp)
         lrs_sort_digits(sfx, digit_bits, t, t.numel() * t.element_size(), keys, None, out, None, n,
                         begin_bit, end_bit, stream)
-        return out
-    fn = globals()["lrs_sort_keys_" + sfx]
-    need = fn(None, 0, keys, out, keys.numel(), begin_bit, end_bit)
-    t = _temp_tensor(need, keys.device, temp)
-    fn(t, t.numel() * t.element_size(), keys, out, keys.numel(), begin_bit, end_bit, stream)
+    else:
+        fn = globals()["lrs_sort_keys_" + sfx]
+        need = fn(None, 0, keys, out, n, begin_bit, end_bit)
+        t = _temp_tensor(need, keys.device, temp)
+        fn(t, t.numel() * t.element_size(), keys, out, n, begin_bit, end_bit, stream)
+    _keep_for(side, t, out, keys if keys is not src else None)
     return out
 
 
 def sort_pairs(keys, values, begin_bit: int = 0, end_bit: int | None = None, keys_out=None,
                values_out=None, temp=None, stream=None, digit_bits: int = 8):
     """Stable ascending pair sort (uint32 values) in passes of `digit_bits` (8
-    or 11) bits; returns (keys_out, values_out)."""
+    or 11) bits; returns (keys_out, values_out).  `values` must hold as many
+    elements as `keys`, and the outputs, when given, must be contiguous with
+    that many elements of the inputs' dtypes on the same device (ValueError
+    otherwise, before any work)."""
     import torch
     sfx = key_suffix(keys.dtype)
     if str(values.dtype) != "torch.uint32":
         raise TypeError("values must be uint32, not %s" % values.dtype)
+    if values.numel() != keys.numel():
+        raise ValueError("values hold %d elements, keys %d" % (values.numel(), keys.numel()))
+    if values.device != keys.device:
+        raise ValueError("values are on %s, keys on %s" % (values.device, keys.device))
     end_bit = KEY_BITS[sfx] if end_bit is None else end_bit
+    ksrc, vsrc = keys, values
     keys = keys.contiguous()
     values = values.contiguous()
+    n = keys.numel()
     if keys_out is None:
         keys_out = torch.empty_like(keys)
+    else:
+        _check_out("keys_out", keys_out, n, keys.dtype, keys.device)
     if values_out is None:
         values_out = torch.empty_like(values)
-    n = keys.numel()
+    else:
+        _check_out("values_out", values_out, n, values.dtype, keys.device)
+    side = _side_stream(stream)
     if digit_bits != 8:
         need = lrs_sort_digits(sfx, digit_bits, None, 0, keys, values, keys_out, values_out, n, begin_bit,
                                end_bit)
         t = _temp_tensor(need, keys.device, temp)
         lrs_sort_digits(sfx, digit_bits, t, t.numel() * t.element_size(), keys, values, keys_out,
                         values_out, n, begin_bit, end_bit, stream)
-        return keys_out, values_out
-    fn = globals()["lrs_sort_pairs_" + sfx]
-    need = fn(None, 0, keys, values, keys_out, values_out, n, begin_bit, end_bit)
-    t = _temp_tensor(need, keys.device, temp)
-    fn(t, t.numel() * t.element_size(), keys, values, keys_out, values_out, n, begin_bit, end_bit, stream)
+    else:
+        fn = globals()["lrs_sort_pairs_" + sfx]
+        need = fn(None, 0, keys, values, keys_out, values_out, n, begin_bit, end_bit)
+        t = _temp_tensor(need, keys.device, temp)
+        fn(t, t.numel() * t.element_size(), keys, values, keys_out, values_out, n, begin_bit, end_bit, stream)
+    _keep_for(side, t, keys_out, values_out, keys if keys is not ksrc else None,
+              values if values is not vsrc else None)
     return keys_out, values_out

@@ -18,6 +18,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <map>
 #include <mutex>
 #include <vector>
@@ -40,7 +41,6 @@ int key_bytes(KeyKind k) { return k == KIND_U64 || k == KIND_I64 || k == KIND_F6
 constexpr int kMaxBlocks = 4096;  // count-matrix width cap (scan: 256 threads x 16)
 constexpr int kWideDigitBits = 11;  // the other digit width lrs_sort_digits takes
 constexpr int kMaxSplit = 8;      // upsweep sub-blocks per downsweep block
-constexpr int kMaxRoute = 16;     // route entries per array: passes + 1 (at most 9)
 constexpr int kUpsweepThreads = 512;
 constexpr int kScanThreads = 256;
 constexpr int kScanPerThread = kMaxBlocks / kScanThreads;
@@ -81,8 +81,14 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // ------------------------------------------------------------------ profiling
 
+// Recording is off unless a benchmark turns it on.  A launch only tests the
+// flag; while it is on, each launch takes the mutex, reserves its record slot
+// (bounds-checked) and records its events under it, so threads that launch
+// concurrently, or that start, read or release the records meanwhile, never
+// share a slot or touch a vector being reassigned.
 struct Prof {
-    bool on = false;
+    std::atomic<bool> on{false};
+    std::mutex mu;
     int cap = 0;
     int count = 0;
     std::vector<hipEvent_t> ev;  // 2 per record
@@ -93,14 +99,18 @@ Prof g_prof;
 template <typename F>
 hipError_t launch(int kind, hipStream_t stream, F &&f)
 {
-    const bool rec = g_prof.on && g_prof.count < g_prof.cap;
-    if (rec) (void)hipEventRecord(g_prof.ev[2 * g_prof.count], stream);
+    if (!g_prof.on.load(std::memory_order_acquire)) {
+        f();
+        return hipGetLastError();
+    }
+    std::lock_guard<std::mutex> lock(g_prof.mu);
+    const int slot = g_prof.on.load(std::memory_order_relaxed) && g_prof.count < g_prof.cap ? g_prof.count++ : -1;
+    if (slot >= 0) (void)hipEventRecord(g_prof.ev[2 * slot], stream);
     f();
-    hipError_t err = hipGetLastError();
-    if (rec) {
-        (void)hipEventRecord(g_prof.ev[2 * g_prof.count + 1], stream);
-        g_prof.kind[g_prof.count] = kind;
-        g_prof.count++;
+    const hipError_t err = hipGetLastError();
+    if (slot >= 0) {
+        (void)hipEventRecord(g_prof.ev[2 * slot + 1], stream);
+        g_prof.kind[slot] = kind;
     }
     return err;
 }
@@ -156,11 +166,16 @@ hipError_t occupancy(const void *kern, int threads, int *per_cu)
 
 // -------------------------------------------------------------------- plan
 
-enum Buf { BUF_IN = 0, BUF_OUT = 1, BUF_A = 2, BUF_B = 3 };
-
+// Which alternate buffers a sort needs in temp storage.  The passes alternate
+// between buffers so that, with no pass skipped, the last one writes the
+// output (the kernels derive each pass's buffers from the same rule, with the
+// skipped passes left out; run_dest in kernels.hpp):
+//  - an array that starts in the input needs A when it runs two passes or more;
+//  - an in-place array (input and output the same memory) goes out to A and
+//    comes back, and with an odd number of passes, three or more, it also uses
+//    B so that its last pass still writes the output (with one pass, the pass
+//    writes A and a copy moves the result back).
 struct Plan {
-    int passes = 0;
-    int dst[64];
     bool need_a = false;
     bool need_b = false;
 };
@@ -168,22 +183,9 @@ struct Plan {
 Plan make_plan(int passes, bool in_place)
 {
     Plan pl;
-    pl.passes = passes;
     if (passes == 0) return pl;
-    if (!in_place || passes % 2 == 0) {
-        for (int p = 0; p < passes; ++p) pl.dst[p] = ((passes - 1 - p) % 2 == 0) ? BUF_OUT : BUF_A;
-        pl.need_a = passes >= 2;
-        return pl;
-    }
-    pl.need_a = true;
-    if (passes == 1) {
-        pl.dst[0] = BUF_A;  // the finalize kernel copies it back
-        return pl;
-    }
-    pl.need_b = true;
-    pl.dst[0] = BUF_A;
-    pl.dst[1] = BUF_B;
-    for (int p = 2; p < passes; ++p) pl.dst[p] = ((passes - 1 - p) % 2 == 0) ? BUF_OUT : BUF_B;
+    pl.need_a = in_place || passes >= 2;
+    pl.need_b = in_place && passes % 2 == 1 && passes >= 3;
     return pl;
 }
 
@@ -211,7 +213,7 @@ struct Layout {
     int64_t tiles = 0;
     int max_cols = 0;  // count-matrix columns (upsweep sub-blocks) at most
     Plan kplan, vplan;
-    size_t off_counts = 0, off_rowtot = 0, off_route = 0, off_spread = 0, off_diff = 0, off_ka = 0, off_kb = 0,
+    size_t off_counts = 0, off_rowtot = 0, off_spread = 0, off_diff = 0, off_ka = 0, off_kb = 0,
            off_va = 0, off_vb = 0;
     size_t total = 0;
 };
@@ -233,8 +235,6 @@ Layout make_layout(const Request &rq)
     off += align_up(radix * L.max_cols * 4);
     L.off_rowtot = off;
     off += align_up(radix * 4);
-    L.off_route = off;  // where keys, then values, are before each pass and at the end
-    off += align_up((size_t)2 * kMaxRoute * 4);
     L.off_spread = off;  // AND and OR of the order codes, per column of the first pass
     off += align_up((size_t)2 * L.max_cols * 8);
     L.off_diff = off;  // their combination over all columns
@@ -258,7 +258,10 @@ lrs_status copy_bytes(void *dst, const void *src, size_t bytes, hipStream_t stre
     if ((d % 16) == 0 && (s % 16) == 0) {
         const int64_t n16 = (int64_t)(bytes / 16);
         if (n16 > 0) {
-            const int grid = (int)std::min<int64_t>((n16 + 255) / 256, 8192);
+            int cus = 0;
+            if (device_cus(&cus) != hipSuccess) return LRS_ERR_HIP;
+            // four 256-thread workgroups per CU (16 waves), one vector per lane per step
+            const int grid = (int)std::min<int64_t>((n16 + 255) / 256, (int64_t)4 * cus);
             err = launch(LRS_KERNEL_COPY, stream, [&] {
                 copy16_kernel<<<grid, 256, 0, stream>>>((const uint4 *)src, (uint4 *)dst, n16);
             });
@@ -293,18 +296,18 @@ struct SpreadArgs {
 };
 
 template <typename K, int CODE, int RB>
-hipError_t launch_upsweep(const SortBufs &bufs, const uint32_t *route, int pass, int src_fixed, uint32_t *counts,
-                          int64_t n, int64_t block_len, int blocks, int shift, uint32_t mask, const SpreadArgs &sp,
+hipError_t launch_upsweep(const SortBufs &bufs, const Route &rt, int pass, uint32_t *counts, int64_t n,
+                          int64_t block_len, int blocks, int shift, uint32_t mask, const SpreadArgs &sp,
                           hipStream_t stream)
 {
     return launch(LRS_KERNEL_UPSWEEP, stream, [&] {
         const int grid = (blocks + kXcds - 1) / kXcds * kXcds;  // see upsweep_kernel's column mapping
         if (sp.spread_out != nullptr)
             upsweep_kernel<K, CODE, kUpsweepThreads, RB, true><<<grid, kUpsweepThreads, 0, stream>>>(
-                bufs, route, pass, src_fixed, counts, n, block_len, blocks, shift, mask, sp.spread_out, sp.diff_in);
+                bufs, rt, pass, counts, n, block_len, blocks, shift, mask, sp.spread_out, sp.diff_in);
         else
             upsweep_kernel<K, CODE, kUpsweepThreads, RB, false><<<grid, kUpsweepThreads, 0, stream>>>(
-                bufs, route, pass, src_fixed, counts, n, block_len, blocks, shift, mask, nullptr, sp.diff_in);
+                bufs, rt, pass, counts, n, block_len, blocks, shift, mask, nullptr, sp.diff_in);
     });
 }
 
@@ -341,23 +344,17 @@ auto downsweep_fn(bool wide)
     }
 }
 
-struct PassRoute {
-    int pass;
-    int ksrc_fixed, vsrc_fixed;  // first pass: where the data is; later passes: -1
-    int kplanned, vplanned;      // planned destinations
-    int last;
-};
-
+// copy_if_idle: this launch (the last pass's) also moves arrays that no pass
+// moved to the output, when no finalize launch follows.
 template <typename K, bool PAIRS, int WAVES, int ITEMS, int CODE, int RB>
-hipError_t launch_downsweep(const SortBufs &bufs, uint32_t *route_k, uint32_t *route_v, const PassRoute &pr,
+hipError_t launch_downsweep(const SortBufs &bufs, const Route &rt, int pass, bool copy_if_idle,
                             const uint32_t *counts, const uint32_t *rowtot, int64_t n, int64_t block_len,
                             int blocks, int cols, int split, int shift, uint32_t mask,
                             const unsigned long long *diff_in, hipStream_t stream)
 {
     return launch(LRS_KERNEL_DOWNSWEEP, stream, [&] {
         downsweep_fn<K, PAIRS, WAVES, ITEMS, CODE, RB>(wide_output<K>(n))<<<blocks, WAVES * 64, 0, stream>>>(
-            bufs, route_k, route_v, pr.pass, pr.ksrc_fixed, pr.vsrc_fixed, pr.kplanned, pr.vplanned, pr.last,
-            counts, rowtot, n, block_len, cols, split, shift, mask, diff_in);
+            bufs, rt, pass, copy_if_idle ? 1 : 0, counts, rowtot, n, block_len, cols, split, shift, mask, diff_in);
     });
 }
 
@@ -409,7 +406,10 @@ lrs_status run_passes(const Request &rq, const Layout &L, char *temp, hipStream_
     const int blocks = (int)((rq.n + block_len - 1) / block_len);
     // The upsweep counts each block as `split` sub-blocks, so that it runs as
     // many workgroups as fill the chip however few blocks the downsweep's
-    // occupancy allows; the count matrix has one column per sub-block.
+    // occupancy allows; the count matrix has one column per sub-block.  The
+    // split doubles while the sub-blocks still fit one round of resident
+    // upsweep workgroups: more columns than that make the scan longer without
+    // a faster upsweep (1e8 keys: 1020 columns sort 6 us faster than 2040).
     int cus = 0, up_per_cu = 0;
     if (device_cus(&cus) != hipSuccess) return LRS_ERR_HIP;
     if (occupancy((const void *)upsweep_kernel<K, CODE, kUpsweepThreads, RB>, kUpsweepThreads, &up_per_cu) !=
@@ -417,38 +417,40 @@ lrs_status run_passes(const Request &rq, const Layout &L, char *temp, hipStream_
         return LRS_ERR_HIP;
     int split = 1;
     while (split < kMaxSplit && (int64_t)blocks * split * 2 <= kMaxBlocks &&
-           (int64_t)blocks * split < (int64_t)cus * up_per_cu)
+           (int64_t)blocks * split * 2 <= (int64_t)cus * up_per_cu)
         split *= 2;
     const int64_t sub_len = block_len / split;  // TILE is a multiple of kMaxSplit
     const int cols = (int)((rq.n + sub_len - 1) / sub_len);
 
     uint32_t *counts = (uint32_t *)(temp + L.off_counts);
     uint32_t *rowtot = (uint32_t *)(temp + L.off_rowtot);
-    uint32_t *route_k = (uint32_t *)(temp + L.off_route);
-    uint32_t *route_v = route_k + kMaxRoute;
     unsigned long long *spread = (unsigned long long *)(temp + L.off_spread);
     unsigned long long *diff = (unsigned long long *)(temp + L.off_diff);
     const SortBufs bufs = sort_bufs<PAIRS>(rq, L, temp);
     // An in-place array starts in the output buffer (the same memory).
-    const int kstart = rq.keys_in == rq.keys_out ? BUF_OUT : BUF_IN;
-    const int vstart = PAIRS && rq.vals_in == rq.vals_out ? BUF_OUT : BUF_IN;
+    Route rt;
+    rt.passes = L.passes;
+    rt.begin_bit = rq.begin_bit;
+    rt.end_bit = rq.end_bit;
+    rt.digit_bits = RB;
+    rt.kstart = rq.keys_in == rq.keys_out ? BUF_OUT : BUF_IN;
+    rt.vstart = PAIRS && rq.vals_in == rq.vals_out ? BUF_OUT : BUF_IN;
+    rt.kb = L.kplan.need_b ? 1 : 0;
+    rt.vb = PAIRS && L.vplan.need_b ? 1 : 0;
+    // Only an in-place array can end outside the output (and then a copy
+    // launch follows the passes); otherwise the last pass's downsweep moves the
+    // data itself when every pass was skipped.
+    const bool finalize = rt.kstart == BUF_OUT || rt.vstart == BUF_OUT;
+    // With more than one pass, the first records the codes' spread, and every
+    // later kernel derives the skipped passes and the route from it.
+    const bool spread_on = L.passes > 1;
 
     for (int p = 0; p < L.passes; ++p) {
         const int shift = rq.begin_bit + RB * p;
         const int width = std::min(RB, rq.end_bit - shift);
         const uint32_t mask = (1u << width) - 1u;
-        PassRoute pr;
-        pr.pass = p;
-        pr.ksrc_fixed = p == 0 ? kstart : -1;
-        pr.vsrc_fixed = p == 0 ? vstart : -1;
-        pr.kplanned = L.kplan.dst[p];
-        pr.vplanned = L.vplan.dst[p];
-        pr.last = p == L.passes - 1;
-
-        // With more than one pass, the first records the codes' spread and the
-        // later ones skip all their work when it shows their digit constant.
         SpreadArgs sp;
-        if (L.passes > 1) {
+        if (spread_on) {
             if (p == 0) {
                 sp.spread_out = spread;
                 sp.diff_out = diff;
@@ -456,20 +458,18 @@ lrs_status run_passes(const Request &rq, const Layout &L, char *temp, hipStream_
                 sp.diff_in = diff;
             }
         }
-        hipError_t err = launch_upsweep<K, CODE, RB>(bufs, route_k, p, pr.ksrc_fixed, counts, rq.n, sub_len, cols,
-                                                     shift, mask, sp, stream);
+        hipError_t err = launch_upsweep<K, CODE, RB>(bufs, rt, p, counts, rq.n, sub_len, cols, shift, mask, sp, stream);
         if (err != hipSuccess) return LRS_ERR_HIP;
         if (launch_scan(counts, rowtot, cols, 1 << RB, shift, mask, sp, stream) != hipSuccess) return LRS_ERR_HIP;
-        err = launch_downsweep<K, PAIRS, WAVES, ITEMS, CODE, RB>(bufs, route_k, route_v, pr, counts, rowtot, rq.n,
-                                                                 block_len, blocks, cols, split, shift, mask,
-                                                                 sp.diff_in, stream);
+        err = launch_downsweep<K, PAIRS, WAVES, ITEMS, CODE, RB>(bufs, rt, p, p == L.passes - 1 && !finalize, counts,
+                                                                 rowtot, rq.n, block_len, blocks, cols, split, shift,
+                                                                 mask, spread_on ? diff : nullptr, stream);
         if (err != hipSuccess) return LRS_ERR_HIP;
     }
-    // The data is in the output unless skipped passes left it elsewhere (or a
-    // one-pass in-place sort went through an alternate buffer).
+    if (!finalize) return LRS_OK;
     const int fin_grid = (int)std::min<int64_t>(((int64_t)sizeof(K) * rq.n + 4095) / 4096, 4096);
     const hipError_t err = launch(LRS_KERNEL_FINALIZE, stream, [&] {
-        finalize_kernel<K, PAIRS><<<fin_grid, 256, 0, stream>>>(bufs, route_k, route_v, L.passes, rq.n);
+        finalize_kernel<K, PAIRS><<<fin_grid, 256, 0, stream>>>(bufs, rt, rowtot, rq.n, spread_on ? diff : nullptr);
     });
     return err == hipSuccess ? LRS_OK : LRS_ERR_HIP;
 }
@@ -693,52 +693,92 @@ LRS_API lrs_status lrs_device_copy(void *d_dst, const void *d_src, size_t bytes,
     return copy_bytes(d_dst, d_src, bytes, stream);
 }
 
+namespace {
+void prof_release_locked()
+{
+    g_prof.on.store(false, std::memory_order_release);
+    for (auto &e : g_prof.ev)
+        if (e) (void)hipEventDestroy(e);
+    g_prof.ev.clear();
+    g_prof.kind.clear();
+    g_prof.cap = 0;
+    g_prof.count = 0;
+}
+}  // namespace
+
+LRS_API lrs_status lrs_bench_read(const void *d_src, size_t bytes, uint32_t *d_result, hipStream_t stream)
+{
+    if (bytes % 16 != 0 || (uintptr_t)d_src % 16 != 0 || (uintptr_t)d_result % 4 != 0) return LRS_ERR_INVALID_ARG;
+    if (bytes > 0 && (!d_src || !d_result)) return LRS_ERR_INVALID_ARG;
+    if (bytes == 0) return LRS_OK;
+    int cus = 0;
+    if (device_cus(&cus) != hipSuccess) return LRS_ERR_HIP;
+    const int64_t n16 = (int64_t)(bytes / 16);
+    // eight 256-thread workgroups per CU: the fastest read measured
+    const int grid = (int)std::min<int64_t>((n16 + 255) / 256, (int64_t)8 * cus);
+    const hipError_t err = launch(LRS_KERNEL_COPY, stream, [&] {
+        read16_kernel<<<grid, 256, 0, stream>>>((const uint4 *)d_src, n16, d_result);
+    });
+    return err == hipSuccess ? LRS_OK : LRS_ERR_HIP;
+}
+
 LRS_API lrs_status lrs_prof_start(int capacity)
 {
     if (capacity <= 0) return LRS_ERR_INVALID_ARG;
-    lrs_prof_release();
+    std::lock_guard<std::mutex> lock(g_prof.mu);
+    prof_release_locked();
     g_prof.ev.assign(2 * (size_t)capacity, nullptr);
     g_prof.kind.assign(capacity, 0);
     for (auto &e : g_prof.ev) {
         if (hipEventCreate(&e) != hipSuccess) {
             e = nullptr;
-            lrs_prof_release();
+            prof_release_locked();
             return LRS_ERR_HIP;
         }
     }
     g_prof.cap = capacity;
     g_prof.count = 0;
-    g_prof.on = true;
+    g_prof.on.store(true, std::memory_order_release);
     return LRS_OK;
 }
 
 LRS_API lrs_status lrs_prof_stop(void)
 {
-    g_prof.on = false;
+    std::lock_guard<std::mutex> lock(g_prof.mu);
+    g_prof.on.store(false, std::memory_order_release);
     return LRS_OK;
 }
 
-LRS_API int lrs_prof_count(void) { return g_prof.count; }
+LRS_API int lrs_prof_count(void)
+{
+    std::lock_guard<std::mutex> lock(g_prof.mu);
+    return g_prof.count;
+}
 
 LRS_API lrs_status lrs_prof_read(int i, int *kind, float *ms)
 {
-    if (i < 0 || i >= g_prof.count || !kind || !ms) return LRS_ERR_INVALID_ARG;
-    if (hipEventSynchronize(g_prof.ev[2 * i + 1]) != hipSuccess) return LRS_ERR_HIP;
+    hipEvent_t a, b;
+    int k;
+    {
+        std::lock_guard<std::mutex> lock(g_prof.mu);
+        if (i < 0 || i >= g_prof.count || !kind || !ms) return LRS_ERR_INVALID_ARG;
+        a = g_prof.ev[2 * i];
+        b = g_prof.ev[2 * i + 1];
+        k = g_prof.kind[i];
+    }
+    // (waits outside the lock; the events stay valid until lrs_prof_release,
+    // which the caller must not run concurrently with a read)
+    if (hipEventSynchronize(b) != hipSuccess) return LRS_ERR_HIP;
     float t = 0.f;
-    if (hipEventElapsedTime(&t, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]) != hipSuccess) return LRS_ERR_HIP;
-    *kind = g_prof.kind[i];
+    if (hipEventElapsedTime(&t, a, b) != hipSuccess) return LRS_ERR_HIP;
+    *kind = k;
     *ms = t;
     return LRS_OK;
 }
 
 LRS_API lrs_status lrs_prof_release(void)
 {
-    for (auto &e : g_prof.ev)
-        if (e) (void)hipEventDestroy(e);
-    g_prof.ev.clear();
-    g_prof.kind.clear();
-    g_prof.on = false;
-    g_prof.cap = 0;
-    g_prof.count = 0;
+    std::lock_guard<std::mutex> lock(g_prof.mu);
+    prof_release_locked();
     return LRS_OK;
 }

@@ -207,3 +207,51 @@ def test_missing_library_fails_loudly(monkeypatch):
         lrs.lrs_sort_keys_u32(None, 0, A, B, 10, 0, 32)
     with pytest.raises(RuntimeError, match="not built"):
         lrs.lrs_sort_digits("u32", 11, None, 0, A, None, B, None, 10, 0, 32)
+
+
+def test_pass_routing_exhaustive(tmp_path):
+    """The route every kernel derives from the skipped passes (kernels.hpp:
+    pass_route, final_buffer, skipped_passes), checked on the host for every
+    pass count up to 12, every set of skipped passes, in place or not:
+    each pass reads where the data is, never writes the input or a buffer the
+    host did not reserve, and the data ends in the output (tests/native/
+    route_check.hip; compiled with hipcc, run on the CPU)."""
+    import shutil
+    import subprocess
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available")
+    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "native", "route_check.hip")
+    exe = str(tmp_path / "route_check")
+    subprocess.check_call([hipcc, "-std=c++17", "-O1", "-o", exe, src], cwd=str(tmp_path),
+                          stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL)
+    res = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert res.returncode == 0, res.stdout + res.stderr
+    assert " 0 failures" in res.stdout
+
+
+def test_convenience_calls_check_sizes_before_any_work():
+    """sort_keys / sort_pairs reject outputs or values whose size, dtype or
+    layout does not match the keys with ValueError, before touching the
+    library (checked with CPU tensors: no device is needed to reach the
+    checks, and none of them may be reached past)."""
+    import torch
+    k = torch.zeros(10, dtype=torch.uint32)
+    v = torch.zeros(10, dtype=torch.uint32)
+    with pytest.raises(ValueError, match="elements"):
+        lrs.sort_keys(k, out=torch.zeros(9, dtype=torch.uint32))
+    with pytest.raises(ValueError, match="dtype"):
+        lrs.sort_keys(k, out=torch.zeros(10, dtype=torch.int32))
+    with pytest.raises(ValueError, match="contiguous"):
+        lrs.sort_keys(k, out=torch.zeros(20, dtype=torch.uint32)[::2])
+    with pytest.raises(ValueError, match="elements"):
+        lrs.sort_pairs(k, torch.zeros(9, dtype=torch.uint32))
+    with pytest.raises(ValueError, match="elements"):
+        lrs.sort_pairs(k, v, values_out=torch.zeros(11, dtype=torch.uint32))
+    with pytest.raises(ValueError, match="elements"):
+        lrs.sort_pairs(k, v, keys_out=torch.zeros(3, dtype=torch.uint32))
+    with pytest.raises(ValueError, match="contiguous"):
+        lrs.sort_pairs(k, v, values_out=torch.zeros(20, dtype=torch.uint32)[::2])
+    # well-formed CPU tensors reach the device check and are refused there
+    with pytest.raises(ValueError, match="device tensors"):
+        lrs.sort_pairs(k, v)

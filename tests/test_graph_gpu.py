@@ -65,14 +65,19 @@ def test_graph_replays_match_eager(key_type, n, pairs, digit_bits):
             assert np.array_equal(got_v, to_host(vout)), "replay %d: values differ" % rep
 
 
-def test_concurrent_calls_on_separate_streams():
+@pytest.mark.parametrize("profiling", [False, True])
+def test_concurrent_calls_on_separate_streams(profiling):
     """Calls from several host threads at once, each on its own stream with its
     own temp storage (the library's per-device caches are shared), each
-    bit-exact with the oracle-checked eager result of its input."""
+    bit-exact with the oracle's result for its input; also with per-launch
+    profiling on (every thread's launches then reserve records under the
+    library's lock, and every record reads back)."""
     import threading
     import torch
     import oracle
-    announce("concurrent calls on separate streams")
+    announce("concurrent calls on separate streams, profiling %s" % profiling)
+    if profiling:
+        lrs.lrs_prof_start(64)  # fewer records than launches: the rest go unrecorded
     cases = [("u32", 300_001, 1), ("f32", 200_003, 2), ("u64", 150_001, 3), ("i32", 250_007, 4)]
     data = {c: inputs.random_keys(c[0], c[1], c[2], "uniform") for c in cases}
     results, errors = {}, []
@@ -91,11 +96,52 @@ def test_concurrent_calls_on_separate_streams():
             errors.append(repr(e))
 
     threads = [threading.Thread(target=work, args=(c,)) for c in cases]
-    for t in threads:
-        t.start()
-    for t in threads:
-        t.join()
+    try:
+        for t in threads:
+            t.start()
+        for t in threads:
+            t.join()
+        if profiling:
+            lrs.lrs_prof_stop()
+            count = lrs.lrs_prof_count()
+            assert count == 64, count
+            for i in range(count):
+                kind, ms = lrs.lrs_prof_read(i)
+                assert kind in lrs.KERNEL_NAMES and ms >= 0.0
+    finally:
+        if profiling:
+            lrs.lrs_prof_release()
     assert not errors, errors
     for c in cases:
         want = oracle.sort_keys(data[c])
         assert np.array_equal(results[c].view(np.uint8), want.view(np.uint8)), c
+
+
+def test_side_stream_outside_stream_context():
+    """sort_keys / sort_pairs on a side stream, called outside any stream
+    context: their temp storage and outputs come from torch's current stream,
+    so they are recorded on the side stream; memory allocated and filled on the
+    current stream right after the calls must not disturb the sorts still
+    running there.  Both results bit-exact with the oracle."""
+    import torch
+    import oracle
+    announce("side stream outside a stream context")
+    keys = inputs.random_keys("u32", 3_000_017, 11, "uniform")
+    vals = np.arange(keys.size, dtype=np.uint32)
+    kin, vin = to_dev(keys), to_dev(vals)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    # a long queue on the side stream, so the sorts are still running when the
+    # current stream reuses freed memory
+    ko = lrs.sort_keys(kin, stream=s)
+    for _ in range(4):
+        ko2, vo2 = lrs.sort_pairs(kin, vin, stream=s)
+    junk = [torch.full((keys.size * 2,), 0x5A5A5A5A, dtype=torch.int32, device="cuda:0") for _ in range(6)]
+    s.synchronize()
+    torch.cuda.synchronize()
+    del junk
+    want_k = oracle.sort_keys(keys)
+    wk, wv = oracle.sort_pairs(keys, vals)
+    assert np.array_equal(to_host(ko), want_k)
+    assert np.array_equal(to_host(ko2), wk)
+    assert np.array_equal(to_host(vo2), wv)

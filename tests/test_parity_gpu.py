@@ -242,18 +242,21 @@ def test_device_copy():
 
 
 def test_profiling_records_every_launch():
+    """Every launch of a sort is recorded: 3 kernels per pass, and a copy
+    launch after the passes only for an in-place sort."""
     import torch
     keys = to_dev(inputs.random_keys("u64", 300_000, 2))
     announce("profiling hooks")
     lrs.lrs_prof_start(64)
     try:
-        lrs.sort_keys(keys)           # 8 passes x 3 kernels, then the finalize check
+        lrs.sort_keys(keys)           # 8 passes x 3 kernels
+        lrs.sort_keys(keys, out=keys)  # in place: then the copy-back check
         torch.cuda.synchronize()
         lrs.lrs_prof_stop()
         recs = [lrs.lrs_prof_read(i) for i in range(lrs.lrs_prof_count())]
     finally:
         lrs.lrs_prof_release()
-    assert [k for k, _ in recs] == [0, 1, 2] * 8 + [4]
+    assert [k for k, _ in recs] == [0, 1, 2] * 8 + [0, 1, 2] * 8 + [4]
     assert all(ms > 0 for _, ms in recs)
 
 
