@@ -79,7 +79,9 @@ typedef enum lrs_status {
     LRS_OK = 0,
     LRS_ERR_INVALID_ARG = 1,
     LRS_ERR_TEMP_TOO_SMALL = 2,
-    LRS_ERR_HIP = 3
+    LRS_ERR_HIP = 3,
+    LRS_ERR_TOO_LARGE = 4  /* lrs_sort_digits_noalloc only: the sort needs more
+                              scratch than the library's static scratch holds */
 } lrs_status;
 
 /* Keys-only sorts: d_keys_in[0..n) -> d_keys_out[0..n). */
@@ -163,6 +165,34 @@ lrs_status lrs_sort_digits(lrs_key_type key_type, int digit_bits, void *d_temp, 
                            const void *d_keys_in, const uint32_t *d_values_in, void *d_keys_out,
                            uint32_t *d_values_out, int64_t n, int begin_bit, int end_bit,
                            hipStream_t stream);
+
+/* The sort of lrs_sort_digits without temp storage from the caller and without
+ * any allocation: for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * The library's count matrix and alternate buffers live instead in one static
+ * device array of LRS_NOALLOC_SCRATCH_BYTES bytes per GPU (held by each GPU
+ * the library runs on until the process ends); the call itself allocates
+ * nothing, on the host or the device.
+ *  - Arguments, results and errors as lrs_sort_digits, without d_temp and
+ *    temp_bytes.
+ *  - A sort whose temp storage (what lrs_sort_digits would ask for with
+ *    d_temp == NULL) exceeds LRS_NOALLOC_SCRATCH_BYTES gives
+ *    LRS_ERR_TOO_LARGE before any device call: at most about 15.6 million
+ *    32-bit keys alone, 7.8 million 32-bit pairs or 64-bit keys, 5.2 million
+ *    64-bit pairs with 8-bit digits (in-place sorts with an odd number of
+ *    passes need twice the alternate space; sorts of up to 16,384 keys and
+ *    begin_bit == end_bit need none).
+ *  - The scratch is shared by every call on a GPU and keeps the last call's
+ *    contents; no part of it needs to start at zero.  Calls that overlap on
+ *    one GPU (other host threads, or other streams before the earlier call's
+ *    work has finished) race on it and give undefined results: serialize
+ *    them on one stream.
+ *  - The first call on a device looks up that device's scratch address
+ *    (hipGetSymbolAddress); it is best made outside any graph capture. */
+#define LRS_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+lrs_status lrs_sort_digits_noalloc(lrs_key_type key_type, int digit_bits, const void *d_keys_in,
+                                   const uint32_t *d_values_in, void *d_keys_out, uint32_t *d_values_out,
+                                   int64_t n, int begin_bit, int end_bit, hipStream_t stream);
 
 /* Static description of a status code (never NULL). */
 const char *lrs_status_string(lrs_status status);

@@ -22,6 +22,8 @@ LRS_OK = 0
 LRS_ERR_INVALID_ARG = 1
 LRS_ERR_TEMP_TOO_SMALL = 2
 LRS_ERR_HIP = 3
+LRS_ERR_TOO_LARGE = 4
+NOALLOC_SCRATCH_BYTES = 64 << 20  # LRS_NOALLOC_SCRATCH_BYTES of include/lrsort.h
 
 KERNEL_NAMES = {0: "upsweep", 1: "scan", 2: "downsweep", 3: "copy", 4: "finalize", 5: "tiny"}
 
@@ -32,7 +34,7 @@ KEY_TYPE_CODES = {"u32": 0, "i32": 1, "f32": 2, "u64": 3, "i64": 4, "f64": 5}
 DIGIT_BITS = (8, 11)
 EXPORTED = SORT_FUNCTIONS + ("lrs_sort_digits", "lrs_status_string", "lrs_device_copy", "lrs_prof_start",
                              "lrs_prof_stop", "lrs_prof_count", "lrs_prof_read",
-                             "lrs_prof_release", "lrs_bench_read")
+                             "lrs_prof_release", "lrs_bench_read", "lrs_sort_digits_noalloc")
 
 
 class LrsError(RuntimeError):
@@ -64,6 +66,8 @@ def load_library() -> ctypes.CDLL:
         fn.restype = ci
     lib.lrs_sort_digits.argtypes = [ci, ci, vp, psz, vp, vp, vp, vp, i64, ci, ci, vp]
     lib.lrs_sort_digits.restype = ci
+    lib.lrs_sort_digits_noalloc.argtypes = [ci, ci, vp, vp, vp, vp, i64, ci, ci, vp]
+    lib.lrs_sort_digits_noalloc.restype = ci
     lib.lrs_status_string.argtypes = [ci]
     lib.lrs_status_string.restype = ctypes.c_char_p
     lib.lrs_device_copy.argtypes = [vp, vp, sz, vp]
@@ -180,6 +184,19 @@ def lrs_sort_digits(key_type, digit_bits, d_temp, temp_bytes, d_keys_in, d_value
                                  int(begin_bit), int(end_bit), st)
     _check(status, "lrs_sort_digits")
     return tb.value
+
+
+def lrs_sort_digits_noalloc(key_type, digit_bits, d_keys_in, d_values_in, d_keys_out, d_values_out, n,
+                            begin_bit, end_bit, stream=None) -> None:
+    """Calls the C function of the same name: lrs_sort_digits with the
+    library's static per-GPU scratch instead of temp storage (no allocation).
+    Raises LrsError (status LRS_ERR_TOO_LARGE) for sorts beyond its size."""
+    lib = load_library()
+    code = KEY_TYPE_CODES[key_type] if isinstance(key_type, str) else int(key_type)
+    status = lib.lrs_sort_digits_noalloc(code, int(digit_bits), _ptr(d_keys_in), _ptr(d_values_in),
+                                         _ptr(d_keys_out), _ptr(d_values_out), int(n), int(begin_bit),
+                                         int(end_bit), _stream(stream))
+    _check(status, "lrs_sort_digits_noalloc")
 
 
 def lrs_device_copy(d_dst, d_src, nbytes: int, stream=None) -> None:

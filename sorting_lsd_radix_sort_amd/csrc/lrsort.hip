@@ -676,6 +676,56 @@ LRS_API lrs_status lrs_sort_digits(lrs_key_type key_type, int digit_bits, void *
     return sort_entry(rq, d_temp, temp_bytes, stream);
 }
 
+// ------------------------------------------------------- allocation-free sort
+
+// The scratch of lrs_sort_digits_noalloc: one array per GPU the library runs
+// on.  In host code `scratch` is only a handle for hipGetSymbolAddress, never
+// a device address: kernels get the per-device address looked up below.
+static __device__ __align__(256) unsigned char scratch[LRS_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[64];  // per device, looked up once
+
+hipError_t scratch_address(void **ptr)
+{
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess) return err;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+}  // namespace
+
+LRS_API lrs_status lrs_sort_digits_noalloc(lrs_key_type key_type, int digit_bits, const void *d_keys_in,
+                                           const uint32_t *d_values_in, void *d_keys_out, uint32_t *d_values_out,
+                                           int64_t n, int begin_bit, int end_bit, hipStream_t stream)
+{
+    // The size query makes every argument check first (no device call).
+    size_t need = 0;
+    lrs_status st = lrs_sort_digits(key_type, digit_bits, nullptr, &need, d_keys_in, d_values_in, d_keys_out,
+                                    d_values_out, n, begin_bit, end_bit, stream);
+    if (st != LRS_OK) return st;
+    // The scratch is 256-byte aligned, so the layout needs none of the 255
+    // bytes of padding the query includes.
+    if (need - (kAlign - 1) > LRS_NOALLOC_SCRATCH_BYTES) return LRS_ERR_TOO_LARGE;
+    if (n == 0) return LRS_OK;  // nothing to do, on the device either
+    void *ptr = nullptr;
+    if (scratch_address(&ptr) != hipSuccess) return LRS_ERR_HIP;
+    size_t bytes = LRS_NOALLOC_SCRATCH_BYTES;
+    return lrs_sort_digits(key_type, digit_bits, ptr, &bytes, d_keys_in, d_values_in, d_keys_out, d_values_out, n,
+                           begin_bit, end_bit, stream);
+}
+
 LRS_API const char *lrs_status_string(lrs_status status)
 {
     switch (status) {
@@ -683,6 +733,9 @@ LRS_API const char *lrs_status_string(lrs_status status)
     case LRS_ERR_INVALID_ARG: return "LRS_ERR_INVALID_ARG: invalid argument";
     case LRS_ERR_TEMP_TOO_SMALL: return "LRS_ERR_TEMP_TOO_SMALL: temp storage smaller than required";
     case LRS_ERR_HIP: return "LRS_ERR_HIP: a HIP call or kernel launch failed";
+    case LRS_ERR_TOO_LARGE:
+        return "LRS_ERR_TOO_LARGE: the sort needs more than the library's static scratch "
+               "(LRS_NOALLOC_SCRATCH_BYTES) holds";
     }
     return "unknown lrs_status";
 }

@@ -255,3 +255,28 @@ def test_convenience_calls_check_sizes_before_any_work():
     # well-formed CPU tensors reach the device check and are refused there
     with pytest.raises(ValueError, match="device tensors"):
         lrs.sort_pairs(k, v)
+
+
+def test_noalloc_rejects_sizes_beyond_its_scratch_before_device_work():
+    """lrs_sort_digits_noalloc checks arguments and its size limit on the host
+    (no device is touched: this runs without a GPU).  Pointers are never
+    dereferenced by these checks."""
+    lib = lrs.load_library()
+    # aligned, far apart (no overlap between the arrays), never dereferenced here
+    fake, kout, vin_p, vout_p = (ctypes.c_void_p(i << 40) for i in (1, 2, 3, 4))
+    nul = ctypes.c_void_p(None)
+    cap = lrs.NOALLOC_SCRATCH_BYTES
+    # 32-bit keys alone: the alternate buffer is 4n bytes; 2^24 keys need 64 MiB + the count matrix
+    for code, ksz, pairs, n in [(0, 4, False, 1 << 24), (0, 4, True, 1 << 23), (3, 8, True, 6 << 20),
+                                (2, 4, False, (cap // 4) + 1)]:
+        st = lib.lrs_sort_digits_noalloc(code, 8, fake, vin_p if pairs else nul, kout, vout_p if pairs else nul,
+                                         n, 0, 8 * ksz, None)
+        assert st == lrs.LRS_ERR_TOO_LARGE, (code, pairs, n, st)
+    assert "scratch" in lrs.status_string(lrs.LRS_ERR_TOO_LARGE)
+    # argument errors come first
+    assert lib.lrs_sort_digits_noalloc(0, 9, fake, nul, fake, nul, 10, 0, 32, None) == lrs.LRS_ERR_INVALID_ARG
+    assert lib.lrs_sort_digits_noalloc(0, 8, fake, nul, fake, nul, 10, 0, 33, None) == lrs.LRS_ERR_INVALID_ARG
+    assert lib.lrs_sort_digits_noalloc(0, 8, nul, nul, fake, nul, 10, 0, 32, None) == lrs.LRS_ERR_INVALID_ARG
+    assert lib.lrs_sort_digits_noalloc(9, 8, fake, nul, fake, nul, 10, 0, 32, None) == lrs.LRS_ERR_INVALID_ARG
+    # nothing to do: no device call either
+    assert lib.lrs_sort_digits_noalloc(0, 8, nul, nul, nul, nul, 0, 0, 32, None) == lrs.LRS_OK
