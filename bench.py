@@ -244,19 +244,29 @@ def main() -> int:
         step()
     torch.cuda.synchronize()
 
-    # ---- timed region: exactly K steps, events on the launch stream
+    # ---- timed region: exactly K steps back to back, one event on the launch
+    # stream before and one after (no event between steps: on small sorts an
+    # event between launches costs a noticeable part of a step)
     log("[bench] timing %d steps" % args.steps)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     torch.cuda.synchronize()
     ev[0].record(stream)
     for i in range(args.steps):
         step()
-        ev[i + 1].record(stream)
+    ev[1].record(stream)
     torch.cuda.synchronize()
-    total_ms = ev[0].elapsed_time(ev[-1])
-    per_step = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    total_ms = ev[0].elapsed_time(ev[1])
     ms_per_step = total_ms / args.steps
     gkeys = n / (ms_per_step * 1e-3) / 1e9
+
+    # ---- the spread of single steps: the same K steps again, an event after each
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record(stream)
+    for i in range(args.steps):
+        step()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per_step = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
 
     # ---- per-kernel durations: same K steps again with events around each launch.
     # Taken before the output check: the check's temporaries (several times the
@@ -285,11 +295,16 @@ def main() -> int:
     torch.cuda.empty_cache()
     log("[bench] output of the last sort equals the first's: %s" % same_again)
 
-    # algorithmic bytes: upsweep reads K*n; downsweep reads and writes (K+V)*n;
-    # the whole sort moves P*(3K+2V)*n (strict reading P*(2K+2V)*n)
-    down_bytes = 2 * (ksz + vsz) * n
-    up_bytes = ksz * n
-    achieved = down_bytes / (avg["downsweep"] * 1e-3) / 1e9
+    # algorithmic bytes per launch: the upsweep reads K*n; the downsweep reads
+    # and writes (K+V)*n; a small sort's one-launch pass does a whole pass,
+    # (3K+2V)*n (its repeated counting reads hit L2, not HBM); the one-workgroup
+    # sort reads and writes the data once, 2(K+V)*n.  The whole sort moves
+    # P*(3K+2V)*n (strict reading P*(2K+2V)*n).
+    per_launch = {"downsweep": 2 * (ksz + vsz) * n, "upsweep": ksz * n,
+                  "small_pass": (3 * ksz + 2 * vsz) * n, "tiny": 2 * (ksz + vsz) * n}
+    dominant = max((k for k in by_kind if k in per_launch), key=lambda k: sum(by_kind[k]))
+    down_bytes = per_launch[dominant]
+    achieved = down_bytes / (avg[dominant] * 1e-3) / 1e9
     sort_bytes = passes * (3 * ksz + 2 * vsz) * n
     strict_bytes = passes * (2 * ksz + 2 * vsz) * n
 
@@ -330,13 +345,13 @@ def main() -> int:
                    "begin_bit": cfg.begin_bit, "end_bit": cfg.end_bit, "passes": passes,
                    "digit_bits": db,
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "downsweep", "achieved": achieved,
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic, "bytes_per_launch": down_bytes,
-                     "avg_launch_ms": avg["downsweep"]},
+                     "traffic": traffic if dominant == "downsweep" else None,
+                     "bytes_per_launch": down_bytes, "avg_launch_ms": avg[dominant]},
         "kernels_avg_ms": avg,
         "kernel_launches": launches,
-        "upsweep_gbs": up_bytes / (avg["upsweep"] * 1e-3) / 1e9,
+        "upsweep_gbs": per_launch["upsweep"] / (avg["upsweep"] * 1e-3) / 1e9 if "upsweep" in avg else None,
         "sort_roofline": {"bytes": sort_bytes, "gbs": sort_bytes / (ms_per_step * 1e-3) / 1e9,
                           "frac": sort_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
                           "strict_bytes": strict_bytes,

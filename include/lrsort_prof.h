@@ -29,7 +29,8 @@ typedef enum lrs_kernel_kind {
     LRS_KERNEL_FINALIZE = 4,   /* after the last pass of a sort with an in-place
                                   array: moves it back to the output if the
                                   passes left it in temp storage */
-    LRS_KERNEL_TINY = 5        /* a whole small sort in one workgroup */
+    LRS_KERNEL_TINY = 5,       /* a whole small sort in one workgroup */
+    LRS_KERNEL_SMALL = 6       /* one whole pass of a small sort in one launch */
 } lrs_kernel_kind;
 
 /* Starts recording with room for `capacity` kernel launches (events are

@@ -25,7 +25,7 @@ LRS_ERR_HIP = 3
 LRS_ERR_TOO_LARGE = 4
 NOALLOC_SCRATCH_BYTES = 64 << 20  # LRS_NOALLOC_SCRATCH_BYTES of include/lrsort.h
 
-KERNEL_NAMES = {0: "upsweep", 1: "scan", 2: "downsweep", 3: "copy", 4: "finalize", 5: "tiny"}
+KERNEL_NAMES = {0: "upsweep", 1: "scan", 2: "downsweep", 3: "copy", 4: "finalize", 5: "tiny", 6: "small_pass"}
 
 KEY_TYPES = ("u32", "i32", "f32", "u64", "i64", "f64")
 SORT_FUNCTIONS = tuple("lrs_sort_keys_" + t for t in KEY_TYPES) + tuple("lrs_sort_pairs_" + t for t in KEY_TYPES)

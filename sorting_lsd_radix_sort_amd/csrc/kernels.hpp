@@ -1362,6 +1362,162 @@ __global__ __launch_bounds__(kWideDigitWaves *kWave)
     }
 }
 
+// ------------------------------------------------- small sorts: one launch a pass
+//
+// Below a few hundred thousand keys a sort is bound by launch latency and
+// kernel-boundary drains, not bandwidth (the page "GPU radix sort: from the
+// CUB implementation to performance tuning", sections 1 and 6, second
+// pitfall: small inputs are dominated by launch overhead).  This pass does the
+// histogram, scan and scatter of one digit in one launch, with no waiting
+// between workgroups: every workgroup reads the whole input of the pass (a
+// few hundred KB, held in L2) and counts its digits itself, those before its
+// own chunk (its prefix) and those from its chunk on (the rest of the
+// totals).  The totals' exclusive prefix gives each digit's start.  It then
+// ranks its chunk of 1024 * ITEMS keys stably, as the downsweep does (ballot
+// match within a wave, per-wave counters that follow input order, a prefix
+// over the waves), and writes each key to digit start + prefix + rank.  The
+// counting is repeated by every workgroup, which is what makes the pass need
+// no upsweep, scan or second launch; it is cheap only while the input is
+// small.
+//
+// Histograms: 32 copies, digit-major with the copy (lane % 32) minor, so the
+// atomics of a wave's lanes fall in distinct banks except lanes l and l + 32.
+constexpr int kSmallCopies = 32;
+
+// Counts the digits of keys [0, n) into two banked histograms: keys before
+// `split` into `before`, the others into `rest` (THREADS lanes striding
+// together, 16-byte loads, four in flight per lane, where the array is 16-byte
+// aligned and `split` a multiple of the keys per vector).
+template <typename K, int CODE, int THREADS>
+__device__ __forceinline__ void count_keys_banked(const K *__restrict__ keys, int n, int split, uint32_t *before,
+                                                  uint32_t *rest, int tid, int shift, uint32_t mask)
+{
+    const int copy = tid & (kSmallCopies - 1);
+    auto add = [&](K k, bool early) {
+        atomicAdd((early ? before : rest) + digit_of<CODE>(k, shift, mask) * kSmallCopies + copy, 1u);
+    };
+    constexpr int PER = 16 / (int)sizeof(K);
+    int from = 0;
+    if ((((uintptr_t)keys & 15) == 0) && split % PER == 0) {
+        const u32x4 *vk = reinterpret_cast<const u32x4 *>(keys);
+        const int ve = n / PER, vsplit = split / PER;
+        constexpr int UNROLL = 4;
+        for (int base = 0; base < ve; base += THREADS * UNROLL) {
+            u32x4 v[UNROLL];
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                const int i = base + u * THREADS + tid;
+                v[u] = i < ve ? vk[i] : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                const int i = base + u * THREADS + tid;
+                if (i < ve) {
+                    const bool early = i < vsplit;
+                    if constexpr (sizeof(K) == 4) {
+                        add((K)v[u].x, early);
+                        add((K)v[u].y, early);
+                        add((K)v[u].z, early);
+                        add((K)v[u].w, early);
+                    } else {
+                        add((K)(((uint64_t)v[u].y << 32) | v[u].x), early);
+                        add((K)(((uint64_t)v[u].w << 32) | v[u].z), early);
+                    }
+                }
+            }
+        }
+        from = ve * PER;
+    }
+    for (int i = from + tid; i < n; i += THREADS) add(keys[i], i < split);
+}
+
+template <typename K, bool PAIRS, int CODE, int ITEMS>
+__global__ __launch_bounds__(1024) void small_pass_kernel(const K *__restrict__ keys_in,
+                                                         const uint32_t *__restrict__ vals_in, K *__restrict__ keys_out,
+                                                         uint32_t *__restrict__ vals_out, int n, int shift, uint32_t mask)
+{
+    constexpr int THREADS = 1024, WAVES = THREADS / kWave;
+    constexpr int CHUNK = THREADS * ITEMS, WAVE_KEYS = kWave * ITEMS;
+    __shared__ uint32_t before[kRadix * kSmallCopies];  // keys before the chunk
+    __shared__ uint32_t rest[kRadix * kSmallCopies];    // keys from the chunk on
+    __shared__ alignas(16) uint16_t wcount[WAVES][kRadix];
+    __shared__ uint32_t base[kRadix];  // output index of the chunk's first key of each digit
+    __shared__ uint32_t scan_tmp[WAVES];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int start = blockIdx.x * CHUNK;
+
+    for (int i = tid; i < kRadix * kSmallCopies; i += THREADS) before[i] = 0u, rest[i] = 0u;
+    for (int i = tid; i < WAVES * kRadix / 2; i += THREADS) reinterpret_cast<uint32_t *>(&wcount[0][0])[i] = 0u;
+    // this chunk's keys (and values), item i of lane l of wave w being key
+    // start + w * WAVE_KEYS + i * 64 + l, so (item, lane) order is input order
+    K k[ITEMS];
+    uint32_t v[PAIRS ? ITEMS : 1];
+    const int first = start + wave * WAVE_KEYS + lane;
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) {
+        const int j = first + i * kWave;
+        k[i] = j < n ? keys_in[j] : (K)0;
+        if constexpr (PAIRS) v[i] = j < n ? vals_in[j] : 0u;
+    }
+    __syncthreads();
+    count_keys_banked<K, CODE, THREADS>(keys_in, n, start, before, rest, tid, shift, mask);
+
+    // rank within the wave, in input order
+    uint32_t r[ITEMS];
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) {
+        const bool valid = first + i * kWave < n;
+        const uint32_t d = digit_of<CODE>(k[i], shift, mask);
+        uint32_t lo, hi;
+        match_digit(d, lo, hi);
+        const uint64_t vm = __ballot(valid);
+        lo &= (uint32_t)vm;
+        hi &= (uint32_t)(vm >> 32);
+        uint16_t *counter = &wcount[wave][d];
+        const uint32_t prior = *counter;
+        // every lane of a digit's group writes the same new count (a lane
+        // past n writes its group's, or the unchanged count)
+        *counter = (uint16_t)(prior + __popc(lo) + __popc(hi));
+        r[i] = lanes_below(lo, hi) + prior;
+    }
+    __syncthreads();
+
+    // thread t < 256, digit t: its count before the chunk and its total (the
+    // copies read from a rotated start, so a wave's lanes spread over the
+    // banks), and the waves' exclusive prefixes within the chunk (in place)
+    uint32_t pre = 0u, all = 0u;
+    if (tid < kRadix) {
+#pragma unroll 8
+        for (int c = 0; c < kSmallCopies; ++c) {
+            pre += before[tid * kSmallCopies + ((c + tid) & (kSmallCopies - 1))];
+            all += rest[tid * kSmallCopies + ((c + tid) & (kSmallCopies - 1))];
+        }
+        all += pre;
+        uint32_t run = 0u;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) {
+            const uint32_t c = wcount[w][tid];
+            wcount[w][tid] = (uint16_t)run;
+            run += c;
+        }
+    }
+    uint32_t total;
+    const uint32_t dstart = block_exclusive_scan<THREADS>(tid < kRadix ? all : 0u, scan_tmp, total);
+    if (tid < kRadix) base[tid] = dstart + pre;
+    __syncthreads();
+
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) {
+        if (first + i * kWave < n) {
+            const uint32_t d = digit_of<CODE>(k[i], shift, mask);
+            const uint32_t pos = base[d] + wcount[wave][d] + r[i];
+            keys_out[pos] = k[i];
+            if constexpr (PAIRS) vals_out[pos] = v[i];
+        }
+    }
+}
+
 // ---------------------------------------------------------------- tiny sorts
 //
 // A sort of at most NMAX keys in one launch and one workgroup, with the keys

@@ -70,6 +70,15 @@ constexpr int kItems = 16;
 constexpr int kSmallItems = 4;
 constexpr int64_t kWideTileMinKeys = (int64_t)1 << 21;
 constexpr int64_t kSmallTileMaxKeys = (int64_t)1 << 17;
+// Sorts of up to kSmallPassMaxBytes of keys (8-bit digits) take one launch per
+// pass (small_pass_kernel), whose workgroups each reread the whole input, 1024
+// keys per workgroup.  Measured on MI355X (uint32 keys / pairs): 65,536 keys in
+// 30 / 33 us against 48 / 54 on the three-kernel path; even at 200,000 keys
+// (58 / 63 against 61 / 70); slower from about 225,000.
+constexpr int64_t kSmallPassMaxBytes = 800000;
+// The one-workgroup sort wins below this many keys (6,144 uint32 keys: 16.9 us
+// against 18.6 for four small passes; 8,192: 20.9 against 19.2).
+constexpr int64_t kTinyMaxKeys = 6144;
 constexpr bool wide_tiles(int kbytes, bool pairs, int64_t n) { return kbytes == 4 && !pairs && n >= kWideTileMinKeys; }
 int tile_keys(KeyKind kind, bool pairs, int64_t n)
 {
@@ -474,6 +483,45 @@ lrs_status run_passes(const Request &rq, const Layout &L, char *temp, hipStream_
     return err == hipSuccess ? LRS_OK : LRS_ERR_HIP;
 }
 
+// Sorts above the one-workgroup limit and up to kSmallPassMaxBytes of keys (8-bit
+// digits): one small_pass_kernel launch per pass, every pass running (a pass
+// over a constant digit reorders nothing, so the result is the same), the
+// buffers alternating as run_dest plans them with no pass skipped.  An
+// in-place array that ends in A is copied back by the device copy.
+template <typename K, bool PAIRS, int CODE, int ITEMS>
+lrs_status run_small_passes(const Request &rq, const Layout &L, char *temp, hipStream_t stream)
+{
+    const SortBufs bufs = sort_bufs<PAIRS>(rq, L, temp);
+    const int kstart = rq.keys_in == rq.keys_out ? BUF_OUT : BUF_IN;
+    const int vstart = PAIRS && rq.vals_in == rq.vals_out ? BUF_OUT : BUF_IN;
+    const bool kb = L.kplan.need_b, vb = PAIRS && L.vplan.need_b;
+    const int grid = (int)((rq.n + 1024 * ITEMS - 1) / (1024 * ITEMS));
+    for (int p = 0; p < L.passes; ++p) {
+        const int shift = rq.begin_bit + kRadixBits * p;
+        const int width = std::min(kRadixBits, rq.end_bit - shift);
+        const uint32_t mask = (1u << width) - 1u;
+        int ks, kd, vs = 0, vd = 0;
+        pass_route(kstart, kb, L.passes, 0u, p, ks, kd);
+        if (PAIRS) pass_route(vstart, vb, L.passes, 0u, p, vs, vd);
+        const hipError_t err = launch(LRS_KERNEL_SMALL, stream, [&] {
+            small_pass_kernel<K, PAIRS, CODE, ITEMS><<<grid, 1024, 0, stream>>>(
+                (const K *)bufs.keys[ks], PAIRS ? bufs.vals[vs] : nullptr, (K *)bufs.keys[kd],
+                PAIRS ? (uint32_t *)bufs.vals[vd] : nullptr, (int)rq.n, shift, mask);
+        });
+        if (err != hipSuccess) return LRS_ERR_HIP;
+    }
+    const int kf = final_buffer(kstart, kb, L.passes, 0u);
+    if (kf != BUF_OUT) {
+        const lrs_status st = copy_bytes(rq.keys_out, bufs.keys[kf], (size_t)rq.n * sizeof(K), stream);
+        if (st != LRS_OK) return st;
+    }
+    if (PAIRS) {
+        const int vf = final_buffer(vstart, vb, L.passes, 0u);
+        if (vf != BUF_OUT) return copy_bytes(rq.vals_out, bufs.vals[vf], (size_t)rq.n * 4, stream);
+    }
+    return LRS_OK;
+}
+
 template <typename K, bool PAIRS, int CODE>
 lrs_status run_tiny(const Request &rq, hipStream_t stream)
 {
@@ -488,11 +536,15 @@ lrs_status run_tiny(const Request &rq, hipStream_t stream)
 template <typename K, int CODE>
 lrs_status run_kind(bool pairs, const Request &r, const Layout &L, char *temp, hipStream_t stream)
 {
-    if (pairs && r.n <= tiny_max<K, true>()) return run_tiny<K, true, CODE>(r, stream);
-    if (!pairs && r.n <= tiny_max<K, false>()) return run_tiny<K, false, CODE>(r, stream);
+    if (pairs && r.n <= std::min<int64_t>(tiny_max<K, true>(), kTinyMaxKeys)) return run_tiny<K, true, CODE>(r, stream);
+    if (!pairs && r.n <= std::min<int64_t>(tiny_max<K, false>(), kTinyMaxKeys)) return run_tiny<K, false, CODE>(r, stream);
     if (r.digit_bits == kWideDigitBits) {
         if (pairs) return run_passes<K, true, kWideDigitWaves, kWideDigitItems, CODE, kWideDigitBits>(r, L, temp, stream);
         return run_passes<K, false, kWideDigitWaves, kWideDigitItems, CODE, kWideDigitBits>(r, L, temp, stream);
+    }
+    if (r.n * (int64_t)sizeof(K) <= kSmallPassMaxBytes) {
+        if (pairs) return run_small_passes<K, true, CODE, 1>(r, L, temp, stream);
+        return run_small_passes<K, false, CODE, 1>(r, L, temp, stream);
     }
     if (r.n <= kSmallTileMaxKeys) {
         if (pairs) return run_passes<K, true, 8, kSmallItems, CODE>(r, L, temp, stream);

@@ -25,7 +25,7 @@ D = 11            # digit width under test
 TILE = 8192       # keys per tile of the 2048-digit downsweep
 CUS = 256
 # largest n sorted by one workgroup (that path ignores the digit width)
-TINY_MAX = {(4, False): 16384, (4, True): 8192, (8, False): 8192, (8, True): 4096}
+TINY_MAX = {(4, False): 6144, (4, True): 6144, (8, False): 6144, (8, True): 4096}
 KEY_TYPES = ["u32", "i32", "f32", "u64", "i64", "f64"]
 RANGES = {"u32": [(0, 32), (0, 11), (0, 22), (0, 23), (3, 17), (5, 27), (21, 32), (31, 32), (5, 5)],
           "i32": [(0, 32), (0, 22), (10, 32), (31, 32)],

@@ -30,10 +30,12 @@ CUS = 256    # compute units of the part: one downsweep workgroup per CU
 
 def tile_of(key_bytes: int, pairs: bool) -> int:
     return 2 * TILE if key_bytes == 4 and not pairs else TILE
-BIG_N = 1 << 17  # above every single-workgroup size limit: the multi-kernel path
+BIG_N = 1 << 18  # above every small-sort limit: the three-kernel path
 # largest n sorted by one workgroup in LDS, per (key bytes, pairs)
-TINY_MAX = {(4, False): 16384, (4, True): 8192, (8, False): 8192, (8, True): 4096}
-SMALL_SIZES = [0, 1, 2, 3, 63, 64, 65, 255, 256, 257, 1023, 1024, 1025, 4095, 4096, 4097,
+TINY_MAX = {(4, False): 6144, (4, True): 6144, (8, False): 6144, (8, True): 4096}
+# largest n sorted by one launch per pass (800,000 bytes of keys), per key bytes
+SMALL_MAX = {4: 200_000, 8: 100_000}
+SMALL_SIZES = [0, 1, 2, 3, 63, 64, 65, 255, 256, 257, 1023, 1024, 1025, 4095, 4096, 4097, 6143, 6144, 6145,
                TILE - 1, TILE, TILE + 1, 2 * TILE, 3 * TILE + 17, 65_536]
 RANGES = {"u32": [(0, 32), (0, 20), (8, 16), (3, 17), (31, 32), (24, 32), (5, 5)],
           "i32": [(0, 32), (0, 20), (16, 32), (31, 32), (28, 32)],
@@ -326,6 +328,37 @@ def test_constant_digit_passes_other_types(key_type):
         announce("constant digits %s %s" % (digits, key_type))
         _compare(keys, vals, 0, bits)
         _compare(keys, vals, 0, bits, in_place_keys=True, in_place_vals=True)
+
+
+@pytest.mark.parametrize("key_type", ["u32", "i32", "f32", "u64", "f64"])
+@pytest.mark.parametrize("pairs", [False, True])
+def test_small_pass_boundary(key_type, pairs):
+    """Both sides of the one-launch-per-pass limit (and its lower end, the
+    one-workgroup limit): uniform, skewed and constant keys, partial bit
+    ranges, and in-place use with odd and even pass counts, element by element
+    against the oracle."""
+    ksz = np.dtype(inputs.KEY_DTYPES[key_type]).itemsize
+    lim = SMALL_MAX[ksz]
+    tiny = TINY_MAX[(ksz, pairs)]
+    bits = 8 * ksz
+    for n in (tiny + 1, tiny + 1023, 65_536, lim - 1, lim, lim + 1):
+        for dist in ("uniform", "and3" if key_type != "f32" else "f32mix"):
+            keys = inputs.random_keys(key_type, n, 9 + n % 97, dist)
+            vals = np.arange(n, dtype=np.uint32) if pairs else None
+            announce("small-pass boundary %s pairs=%s n=%d dist=%s" % (key_type, pairs, n, dist))
+            _compare(keys, vals, 0, bits)
+        _compare(keys, vals, 3, bits - 5)
+    n = lim - 5
+    keys = np.full(n, 0x5A, dtype=inputs.KEY_DTYPES[key_type])
+    vals = np.arange(n, dtype=np.uint32) if pairs else None
+    announce("small-pass constant keys %s pairs=%s" % (key_type, pairs))
+    _compare(keys, vals, 0, bits)
+    keys = inputs.random_keys(key_type, n, 31, "dup")
+    for b, e in [(0, 8), (0, 16), (0, 24), (4, 9), (0, bits)]:
+        announce("small-pass in-place %s pairs=%s bits=[%d,%d)" % (key_type, pairs, b, e))
+        _compare(keys, vals, b, e, in_place_keys=True, in_place_vals=pairs)
+        if pairs:
+            _compare(keys, vals, b, e, in_place_keys=False, in_place_vals=True)
 
 
 @pytest.mark.parametrize("key_type", ["u32", "f32", "u64", "f64"])

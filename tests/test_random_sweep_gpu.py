@@ -21,7 +21,8 @@ pytestmark = pytest.mark.gpu
 KEY_TYPES = ["u32", "i32", "f32", "u64", "i64", "f64"]
 # sizes where the path changes: the one-workgroup limits, the small-tile
 # bound, the 16-wave shape's threshold, and tile multiples
-EDGES = [1, 2, 4095, 4096, 8192, 8193, 16384, 16385, 1 << 17, (1 << 17) + 1, (1 << 21) - 1, 1 << 21,
+EDGES = [1, 2, 4095, 4096, 6144, 6145, 8192, 8193, 16384, 16385, 100_000, 100_001, 1 << 17, (1 << 17) + 1,
+         200_000, 200_001, (1 << 21) - 1, 1 << 21,
          (1 << 21) + 1, 16384 * 130 + 5, 8192 * 300 - 1]
 CASES = 120
 

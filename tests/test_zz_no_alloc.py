@@ -57,7 +57,7 @@ def same(a, b):
     ("f32", True, 8, (0, 32), (1_500_007, 70_001)),
     ("u64", True, 8, (0, 64), (1_000_003, 30_011)),
     ("i32", False, 11, (0, 32), (2_000_003, 17_000)),       # 2048-digit passes
-    ("u32", True, 8, (0, 20), (7_000_001, 16_384)),          # near the limit, then the one-workgroup path
+    ("u32", True, 8, (0, 20), (7_000_001, 16_384)),          # near the limit, then one launch per pass
     ("f64", False, 8, (3, 41), (2_500_001, 400_009)),
 ])
 def test_noalloc_matches_sort_digits(key_type, pairs, digit_bits, bits, sizes):
