@@ -26,7 +26,6 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published peak
 PAGES_GPU_GKEYS = 6.25         # 1e8 32-bit ints in ~16 ms (quant67.com survey, sections 9.3-9.4)
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "downsweep_traffic.txt")
 
 
 def log(msg: str) -> None:
@@ -61,21 +60,23 @@ def kernel_source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per downsweep launch from the committed rocprofv3 counter
-    summary, if it was taken on this workload with the current kernel source."""
+def measured_traffic(workload: str, digit_bits: int, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary of this workload (profiles/<workload>[_d11]_traffic.txt), if it was
+    taken with the current kernel source; None otherwise."""
+    path = os.path.join(ROOT, "profiles", "%s%s_traffic.txt" % (workload, "_d11" if digit_bits == 11 else ""))
     try:
         fields = {}
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             for ln in f:
                 if ":" in ln and not ln.startswith("#"):
                     k, v = ln.split(":", 1)
                     fields[k.strip()] = v.strip()
         if fields.get("kernel_source_digest") != kernel_source_digest():
             return None
-        if fields.get("workload") != workload:
+        if fields.get("workload") != workload or int(fields.get("digit_bits", "0")) != digit_bits:
             return None
-        return float(fields["traffic_bytes_per_launch"])
+        return float(fields["traffic." + kernel])
     except (OSError, KeyError, ValueError):
         return None
 
@@ -148,6 +149,8 @@ def main() -> int:
                     help="keys of the input the CPU oracle sorts for the baseline (0: all of them)")
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ref-reps", type=int, default=400,
+                    help="launches of each streaming reference (copy, read) timed before the warmup")
     ap.add_argument("--digit-bits", type=int, default=8, choices=(8, 11),
                     help="digit width of the passes (11: lrs_sort_digits with 2048-digit passes)")
     args = ap.parse_args()
@@ -216,7 +219,7 @@ def main() -> int:
     # before the sorts' warmup: their ~100 ms of back-to-back kernels also bring
     # the GPU out of its idle clock state (kernels run ~10 % slower for the first
     # ~20 ms after an idle spell), so the warmup sorts start at working clocks.
-    ref_reps = 400
+    ref_reps = max(1, args.ref_reps)
 
     def time_ref(fn):
         ev2 = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
@@ -309,7 +312,6 @@ def main() -> int:
     strict_bytes = passes * (2 * ksz + 2 * vsz) * n
 
     workload = cfg.name
-    traffic = measured_traffic(workload) if db == 8 else None
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -347,7 +349,7 @@ def main() -> int:
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic if dominant == "downsweep" else None,
+                     "traffic": measured_traffic(workload, db, dominant),
                      "bytes_per_launch": down_bytes, "avg_launch_ms": avg[dominant]},
         "kernels_avg_ms": avg,
         "kernel_launches": launches,

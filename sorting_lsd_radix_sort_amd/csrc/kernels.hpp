@@ -283,7 +283,9 @@ __device__ __forceinline__ void grid_copy(const T *__restrict__ src, T *__restri
         const int64_t nv = n / PER;
         const u32x4 *s4 = reinterpret_cast<const u32x4 *>(src);
         u32x4 *d4 = reinterpret_cast<u32x4 *>(dst);
-        for (int64_t i = first; i < nv; i += stride) d4[i] = __builtin_nontemporal_load(&s4[i]);
+        // non-temporal both ways: whole 16-byte vectors, written once
+        for (int64_t i = first; i < nv; i += stride)
+            __builtin_nontemporal_store(__builtin_nontemporal_load(&s4[i]), &d4[i]);
         done = nv * PER;
     }
     for (int64_t i = done + first; i < n; i += stride) dst[i] = src[i];
