@@ -180,8 +180,7 @@ lrs_status lrs_sort_digits(lrs_key_type key_type, int digit_bits, void *d_temp, 
  *    LRS_ERR_TOO_LARGE before any device call: at most about 15.6 million
  *    32-bit keys alone, 7.8 million 32-bit pairs or 64-bit keys, 5.2 million
  *    64-bit pairs with 8-bit digits (in-place sorts with an odd number of
- *    passes need twice the alternate space; sorts of up to 16,384 keys and
- *    begin_bit == end_bit need none).
+ *    passes, three or more, need twice the alternate space).
  *  - The scratch is shared by every call on a GPU and keeps the last call's
  *    contents; no part of it needs to start at zero.  Calls that overlap on
  *    one GPU (other host threads, or other streams before the earlier call's

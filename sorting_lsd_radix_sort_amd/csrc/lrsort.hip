@@ -46,8 +46,9 @@ constexpr int kScanThreads = 256;
 constexpr int kScanPerThread = kMaxBlocks / kScanThreads;
 constexpr size_t kAlign = 256;
 
-// Sorts of at most tiny_max keys run in one launch of one workgroup with the
-// data in LDS (tiny_sort_kernel): two copies of the keys and values in 128 KB.
+// The most keys the one-workgroup sort (tiny_sort_kernel) can hold: two
+// copies of the keys and values in 128 KB of LDS.  It is used up to the
+// smaller of this and kTinyMaxKeys.
 template <typename K, bool PAIRS>
 constexpr int tiny_max()
 {
