@@ -1,8 +1,9 @@
 """A seeded random sweep over the sort's argument space, on cuda:0.
 
 Each case draws every argument at once: key type, keys alone or pairs, n
-(log-uniform up to 4M, or next to a size where the kernel shapes change), bit
-range, key distribution, digit width and in-place use of keys and values.
+(log-uniform up to 4M, or at or next to a size where the kernel shapes or the
+path change), bit range, key distribution, digit width and in-place use of
+keys and values.
 The result is compared element by element with the oracle.  The cases come
 from a fixed seed, so a failure names a case that can be run again by its
 index.
@@ -21,10 +22,12 @@ pytestmark = pytest.mark.gpu
 KEY_TYPES = ["u32", "i32", "f32", "u64", "i64", "f64"]
 # sizes where the path changes: the one-workgroup limits, the small-tile
 # bound, the 16-wave shape's threshold, and tile multiples
-EDGES = [1, 2, 4095, 4096, 6144, 6145, 8192, 8193, 16384, 16385, 100_000, 100_001, 1 << 17, (1 << 17) + 1,
-         200_000, 200_001, (1 << 21) - 1, 1 << 21,
-         (1 << 21) + 1, 16384 * 130 + 5, 8192 * 300 - 1]
-CASES = 120
+EDGES = [1, 2, 3, 63, 64, 65, 1023, 1024, 1025, 4095, 4096, 6143, 6144, 6145, 8192, 8193, 16384, 16385,
+         99_999, 100_000, 100_001, (1 << 17) - 1, 1 << 17, (1 << 17) + 1, 199_999, 200_000, 200_001,
+         (1 << 21) - 1, 1 << 21, (1 << 21) + 1, 16384 * 130 + 5, 8192 * 300 - 1,
+         # a block of 24 tiles split in 4 columns, plus one key; a ragged last column
+         16384 * 24 * 3 + 1, 393216 * 4 - 7]
+CASES = 300
 
 
 def _case(i):
